@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP8 m<=8 GEMM + Lamport publish + collect on one MI355X.
+
+One step is one pass of the whole hot path over one call's inputs: the GEMM
+with its BF16 publish into the mailbox (mxgemm_publish) and the collect that
+empties the mailbox (mailbox_collect). The workload is N=7168, K=8192, m=8,
+split-K 4, one rank slot, W ~ N(0, 0.02) and x ~ N(0, 1) with 1 % of channels
+x50, MXFP8-quantized per 32 (seeded). Inputs are resident in HBM before the
+timed region; every step reads one of ceil(512 MiB / |W|) copies of W and its
+scales in turn, so W comes from HBM and not from the 256 MiB Infinity Cache.
+
+Printed (one JSON line): whole-step throughput in algorithmic GB/s, ms per
+step, the GEMM kernel's roofline (algorithmic bytes / its mean duration from
+HIP events recorded around the kernel itself, vs the 8 TB/s HBM peak), a
+graph-replay figure, the parity of the final output against the CPU oracle,
+and the oracle's own time on the host (cpu_baseline).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--dist outliers]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("µs/call and achieved HBM GB/s (fraction of peak), MXFP8 m≤8 "
+          "GEMM+publish")
+HBM_PEAK_GBS = 8000.0
+COLD_BYTES = 512 * 2**20
+
+
+def parse() -> argparse.Namespace:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--dist", default="outliers", choices=["outliers", "normal"])
+    ap.add_argument("--warm", action="store_true", help="one W copy (Infinity-Cache resident)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-calls", type=int, default=3)
+    return ap.parse_args()
+
+
+def cpu_baseline(problem, calls: int) -> tuple[dict, object]:
+    """Time the CPU oracle on the same workload (test infrastructure, timed
+    here only as a reported baseline)."""
+    import numpy as np
+
+    from oracle import gemm, mailbox
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    times = []
+    result = None
+    for _ in range(calls):
+        t0 = time.perf_counter()
+        bits, exact, abs_sum = gemm.gemm_publish_bits(problem.w, problem.ws, problem.x,
+                                                      problem.xs)
+        mb = mailbox.MailboxModel(1, 114688)
+        mb.publish(0, bits)
+        out = mb.collect(problem.out_bytes)
+        times.append(time.perf_counter() - t0)
+        result = (bits, exact, abs_sum, out)
+    sec = float(np.median(times))
+    cpu = {
+        "value": round(problem.algorithmic_bytes() / sec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{calls} full calls of the same N=7168 K=8192 m=8 workload (dequantize, "
+                   f"float64 GEMM, BF16 RNE, -0 clear, mailbox publish+collect model); "
+                   f"median {sec:.3f} s per call"),
+    }
+    return cpu, result
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the multi-GPU exchange is design only)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from mxfp8_decode_gemm_amd import binding as mx
+    from mxfp8_decode_gemm_amd import device as dv
+    from workloads import generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    p = generate.config_problem(2, dist=args.dist)
+    split_k = p.split_k
+    wbytes = p.w.nbytes + p.ws.nbytes
+    copies = 1 if args.warm else max(1, -(-COLD_BYTES // wbytes))
+    w0 = dv.upload(p.w, dev)
+    ws0 = dv.upload(p.ws, dev)
+    ws_copies = [(w0, ws0)] + [(w0.clone(), ws0.clone()) for _ in range(copies - 1)]
+    x = dv.upload(p.x, dev)
+    xs = dv.upload(p.xs, dev)
+    mbx = dv.Mailbox(1, 114688, device=dev)
+    wsp = dv.Workspace(p.n, split_k, device=dev)
+    out = torch.empty(p.m * p.n, dtype=torch.int16, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    nbytes = p.out_bytes
+
+    def step(i, ev=None):
+        w, ws = ws_copies[i % copies]
+        if ev is None:
+            mx.mxgemm_publish(mbx.mb, w, ws, x, xs, p.m, p.n, p.k, split_k, wsp.buf,
+                              wsp.nbytes, None, stream)
+        else:
+            mx.mxgemm_publish_timed(mbx.mb, w, ws, x, xs, p.m, p.n, p.k, split_k, wsp.buf,
+                                    wsp.nbytes, None, stream, ev[0], ev[1])
+        mx.mailbox_collect(mbx.mb, out, nbytes, stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        stream.synchronize()
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in kev:  # materialize the event handles
+            a.record(stream)
+            b.record(stream)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i, kev[i])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = t0.elapsed_time(t1) / args.steps
+        kern_ms = [a.elapsed_time(b) for a, b in kev]
+
+        # Same loop captured once as a HIP graph and replayed.
+        mx.mxg_graph_begin(stream)
+        for i in range(args.steps):
+            step(i)
+        graph = mx.mxg_graph_end(stream)
+        mx.mxg_graph_launch(graph, stream)  # warm replay
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        mx.mxg_graph_launch(graph, stream)
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms_step = g0.elapsed_time(g1) / args.steps
+        mx.mxg_graph_destroy(graph)
+        calls = args.warmup + 3 * args.steps
+        st = mbx.state_words()
+        hdr = wsp.header()
+    got = dv.as_u16(out).reshape(p.m, p.n)
+
+    algo = p.algorithmic_bytes()
+    kern_mean = float(np.mean(kern_ms))
+    achieved = algo / (kern_mean * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(algo / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "N=7168 K=8192 m=8 split-K 4 MXFP8 (e4m3 + E8M0/32) GEMM, BF16 "
+                        "publish into a 1-slot 3-generation Lamport mailbox, then collect",
+            "n": p.n, "k": p.k, "m": p.m, "split_k": split_k, "ranks": 1,
+            "dist": args.dist, "seed": p.seed, "w_copies": copies,
+            "algorithmic_bytes_per_call": algo,
+        },
+        "us_per_call": round(ms_step * 1e3, 3),
+        "graph_us_per_call": round(graph_ms_step * 1e3, 3),
+        "gemm_kernel_us": {"mean": round(kern_mean * 1e3, 3),
+                           "min": round(min(kern_ms) * 1e3, 3),
+                           "max": round(max(kern_ms) * 1e3, 3)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "state_ok": bool(st[mx.STATE_NEXT] == calls % 3 and st[mx.STATE_ERROR] == 0
+                         and hdr[mx.WS_EPOCH] == 1 + calls and hdr[mx.WS_ERROR] == 0),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import codecs, tolerance
+
+        cpu, (bits, exact, abs_sum, _) = cpu_baseline(p, args.cpu_calls)
+        line["cpu_baseline"] = cpu
+        ex = tolerance.excess(got, exact, abs_sum)
+        same = codecs.bf16_to_f64(got) == codecs.bf16_to_f64(bits)
+        line["parity"] = {"within_tolerance": bool(np.all(ex <= 1.0)),
+                          "max_excess": round(float(ex.max()), 4),
+                          "bits_equal_oracle_frac": round(float(same.mean()), 5),
+                          "no_negative_zero": bool(not np.any(got == 0x8000))}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

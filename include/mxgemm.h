@@ -1,0 +1,203 @@
+/*
+ * mxgemm.h -- C ABI of the MI355X (gfx950) low-batch MXFP8 publishing GEMM and
+ * its three-generation Lamport mailbox.
+ *
+ * Page citations name the four API pages by module:
+ *   "all_gather page"      vllm.models.deepseek_v41.nvidia.ops.cute_dsl.all_gather
+ *   "publishing_gemm page" vllm.models.deepseek_v41.nvidia.specialized_decode.
+ *                          boundary.publishing_gemm
+ *   "sync page"            vllm.models.deepseek_v41.amd.mono.common.sync
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers are HIP device memory owned by the
+ *     caller; the library never allocates, frees or keeps them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *     work is enqueued on it; no entry point synchronizes the host, so every
+ *     call except mailbox_init and mxgemm_workspace_init may be captured into
+ *     a HIP graph.
+ *   - Arguments are validated on the host from sizes and addresses alone
+ *     (all_gather page, LamportAllGather.accepts: decided from the size, so
+ *     every caller decides alike). On any error nothing is enqueued and a
+ *     negative MXG_E* code is returned; 0 means enqueued.
+ *   - Calls on one mailbox go on one stream, in order, and never overlap
+ *     (all_gather page, module docstring, closing paragraph).
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------ */
+#define MXG_OK 0
+#define MXG_EINVAL (-1)       /* null pointer, bad shape or rank, bad split_k */
+#define MXG_EALIGN (-2)       /* a pointer is not 16-byte aligned */
+#define MXG_ECAPACITY (-3)    /* payload does not fit a rank slot */
+#define MXG_EWORKSPACE (-4)   /* split-K workspace missing or too small */
+#define MXG_EUNSUPPORTED (-5) /* valid, but no kernel variant takes it: fall back */
+#define MXG_EHIP (-6)         /* a HIP call failed (no device, launch error) */
+
+/* ---- mailbox geometry (all_gather page, module docstring) --------------- */
+#define MXG_GENERATIONS 3     /* three generations */
+#define MXG_PACK_BYTES 16     /* handled in 16-byte packs */
+#define MXG_SENTINEL 0x80000000u /* idle word: FP32 -0 / INT32_MIN */
+#define MXG_MAX_RANKS 8
+#define MXG_MAX_ROWS 8        /* at most 8 activation rows (publishing_gemm page) */
+#define MXG_SCALE_BLOCK 32    /* one E8M0 scale per 32 K (sf_vec_size=32) */
+
+/* Mailbox state words (uint32). NEXT and ACTIVE are the stage words of the
+ * publishing_gemm page's module docstring: [0] the generation the next
+ * publish writes (advanced by the collect that empties it), [1] the
+ * generation the last publish wrote. COLLECT_ARR counts collect workgroups
+ * (all_gather page, step 3: the last to arrive advances the generation).
+ * ERROR is a sticky bit set: MXG_ERR_* below. */
+#define MXG_STATE_WORDS 8
+#define MXG_STATE_NEXT 0
+#define MXG_STATE_ACTIVE 1
+#define MXG_STATE_COLLECT_ARR 2
+#define MXG_STATE_ERROR 3
+
+/* Split-K workspace header (uint32 words at the start of the workspace).
+ * EPOCH tags every (value, tag) pair a GEMM call exchanges between its
+ * workgroups (sync page, Mailbox docstring: a launch tags its hand-offs with
+ * its epoch, so a pair from an earlier call never carries a live tag). */
+#define MXG_WS_HEADER_BYTES 256
+#define MXG_WS_EPOCH 0
+#define MXG_WS_ARRIVALS 1
+#define MXG_WS_ERROR 2
+
+#define MXG_ERR_COLLECT_SPIN 0x1u /* a collect gave up polling a slot */
+#define MXG_ERR_SPLITK_SPIN 0x2u  /* a split-K owner gave up polling its pairs */
+
+/* Host-side descriptor of one mailbox (plain data, copied freely). */
+typedef struct mxg_mailbox {
+  void* slots;             /* device: 3 * ranks * capacity_bytes, 16-B aligned */
+  uint32_t* state;         /* device: MXG_STATE_WORDS words, 16-B aligned */
+  int32_t ranks;           /* emulated rank slots, 1..8 */
+  int32_t rank;            /* the slot mxgemm_publish writes, 0..ranks-1 */
+  int64_t capacity_bytes;  /* bytes per rank slot, > 0, multiple of 16 */
+} mxg_mailbox;
+
+/* Bytes of slot memory a mailbox needs: 3 * ranks * capacity_bytes, or 0 if
+ * the arguments are invalid. */
+size_t mxg_mailbox_slots_bytes(int32_t ranks, int64_t capacity_bytes);
+
+/* Fill `mb` and arm the mailbox: every slot word becomes the sentinel,
+ * NEXT = ACTIVE = COLLECT_ARR = ERROR = 0 (all_gather page,
+ * LamportAllGather.__init__: the mailbox starts as the sentinel with a zero
+ * state). Enqueues fill kernels on `stream`; call it at a quiescent point,
+ * outside graph capture. Errors: MXG_EINVAL (null, ranks outside 1..8, rank
+ * outside 0..ranks-1, capacity not a positive multiple of 16), MXG_EALIGN,
+ * MXG_EHIP. */
+int mailbox_init(mxg_mailbox* mb, void* slots, uint32_t* state, int32_t ranks,
+                 int32_t rank, int64_t capacity_bytes, void* stream);
+
+/* Bytes of split-K workspace mxgemm_publish needs for these sizes: 0 when
+ * split_k == 1, else MXG_WS_HEADER_BYTES + split_k * 64 * ceil(n/8)*8: eight
+ * (value, tag) pairs of 8 bytes for each of 8 token rows and n/8 packs. */
+size_t mxgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t split_k);
+
+/* Arm a workspace: zero every pair, EPOCH = 1, ARRIVALS = ERROR = 0. Call it
+ * once before first use, outside capture; a workspace may then serve calls
+ * of any size up to its capacity, in any order. Errors: MXG_EINVAL,
+ * MXG_EALIGN, MXG_EHIP. */
+int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* The publishing GEMM (publishing_gemm page, module docstring, "GEMM
+ * structure"; PublishingLowLatencyBlockscaledGemmKernel.epilog_warp and
+ * publish_value):
+ *
+ *   C[t, n] = sum_k dec(w[n,k]) 2^(w_scale[n,k/32]-127)
+ *                   dec(x[t,k]) 2^(x_scale[t,k/32]-127)
+ *
+ * accumulated in FP32, rounded to BF16 (nearest even), negative zero cleared,
+ * and stored as [m, n] row-major BF16 into bytes [0, 2mn) of slot mb->rank of
+ * generation state[NEXT], in 16-byte packs of eight consecutive columns of one
+ * token (even column in the low half of each word). One thread then sets
+ * state[ACTIVE] = that generation.
+ *
+ *   w        device, [n, k] e4m3fn bytes, row-major (k contiguous), 16-B aligned
+ *   w_scale  device, [n, k/32] E8M0 bytes, row-major, 16-B aligned
+ *   x        device, [m, k] e4m3fn bytes, row-major, 16-B aligned
+ *   x_scale  device, [m, k/32] E8M0 bytes, row-major, 16-B aligned
+ *   m        activation rows, 1..8
+ *   n, k     n % 8 == 0, k % 128 == 0, k % (128 * split_k) == 0
+ *   split_k  1, 2, 4 or 8: K is cut into split_k slices; the workgroups of one
+ *            output tile exchange FP32 partials through (value, epoch) pairs
+ *            in `workspace` and each reduces its share of the tile's packs,
+ *            summing the slices in ascending K order.
+ *   workspace, workspace_bytes  device, at least mxgemm_workspace_bytes(),
+ *            armed by mxgemm_workspace_init; may be NULL/0 when split_k == 1.
+ *            One call at a time per workspace.
+ *   c_out    device or NULL: [m, n] BF16 as rounded, before the negative-zero
+ *            clearing (the plain output of the linear), 16-B aligned.
+ *
+ * Every publish must be followed by exactly one mailbox_collect of 2*m*n
+ * bytes before the next publish into the same mailbox (publishing_gemm page,
+ * PublishingMxfp8Linear.precompile: a publish without its consumer would
+ * desynchronize the mailbox). Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY
+ * (2mn > capacity), MXG_EWORKSPACE, MXG_EUNSUPPORTED (the split-K grid cannot
+ * be co-resident on this device), MXG_EHIP. */
+int mxgemm_publish(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                   const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n,
+                   int32_t k, int32_t split_k, void* workspace,
+                   size_t workspace_bytes, uint16_t* c_out, void* stream);
+
+/* mxgemm_publish for measurement: identical arguments and effects, plus two
+ * hipEvent_t (as void*, both required) that HIP records around the GEMM
+ * kernel's own execution (hipExtLaunchKernel), so hipEventElapsedTime gives
+ * the kernel's duration without launch gaps. Not capturable into a graph.
+ * Errors: those of mxgemm_publish; MXG_EINVAL if an event is NULL. */
+int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                         const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n,
+                         int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
+                         uint16_t* c_out, void* stream, void* ev_start, void* ev_stop);
+
+/* Unfused publish: copy `nbytes` of BF16 from `src` (device, 16-B aligned)
+ * into slot `rank` of generation state[NEXT] with negative zero cleared, and
+ * set state[ACTIVE]. Serves as the emulated peers' publish and as the
+ * unfused path the fused epilogue must match bit for bit (publishing_gemm
+ * page, module docstring: the consumer sees the same bits either way).
+ * Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY (nbytes outside
+ * (0, capacity] or not a multiple of 16), MXG_EHIP. */
+int mailbox_publish(const mxg_mailbox* mb, int32_t rank, const void* src,
+                    int64_t nbytes, void* stream);
+
+/* Collect (all_gather page, module docstring, step 2; _AllGatherKernel.kernel):
+ * for every rank r and pack p < nbytes/16 of generation g = state[NEXT],
+ * poll the pack until none of its four words is the sentinel, write it to
+ * out + (r * nbytes + 16 p) (rank-major: [ranks*m, n] for an [m, n]
+ * payload), and store the sentinel back. The last workgroup to finish sets
+ * state[NEXT] = (g + 1) mod 3 (step 3). A pack still holding a sentinel after
+ * the spin limit is copied as it is and MXG_ERR_COLLECT_SPIN is set in
+ * state[ERROR]. `out` is device memory of ranks * nbytes bytes, 16-B aligned.
+ * Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY, MXG_EHIP. */
+int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream);
+
+/* Poll limit of the device spin loops (collect and split-K), in polls; the
+ * loops back off with s_sleep between polls. Returns the previous limit.
+ * A limit of 0 restores the default (2^20 polls). Process-wide. */
+uint32_t mxg_set_spin_limit(uint32_t polls);
+
+/* HIP graph helpers: capture the calls issued on `stream` between begin and
+ * end into an executable graph, replay it, destroy it. `exec` is an opaque
+ * hipGraphExec_t. Kernels must have been launched once before capture
+ * (publishing_gemm page, PublishingMxfp8Linear.precompile: compile before
+ * capture). Errors: MXG_EINVAL, MXG_EHIP. */
+int mxg_graph_begin(void* stream);
+int mxg_graph_end(void* stream, void** exec);
+int mxg_graph_launch(void* exec, void* stream);
+int mxg_graph_destroy(void* exec);
+
+/* Static string describing a return code. */
+const char* mxg_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

@@ -1,0 +1,249 @@
+"""ctypes binding of libmxgemm.so: the C ABI of include/mxgemm.h, same names.
+
+Argument marshalling only: every step of the hot path runs in the HIP
+library. Device buffers may be passed as torch tensors (their data_ptr is
+used) or as integer device addresses; streams as torch streams, raw
+hipStream_t integers or None (torch's current stream). Importing this module
+loads the library and raises if it has not been built: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmxgemm.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mxgemm.h")
+
+OK = 0
+EINVAL = -1
+EALIGN = -2
+ECAPACITY = -3
+EWORKSPACE = -4
+EUNSUPPORTED = -5
+EHIP = -6
+
+GENERATIONS = 3
+PACK_BYTES = 16
+SENTINEL = 0x80000000
+MAX_RANKS = 8
+MAX_ROWS = 8
+STATE_WORDS = 8
+STATE_NEXT, STATE_ACTIVE, STATE_COLLECT_ARR, STATE_ERROR = 0, 1, 2, 3
+WS_HEADER_BYTES = 256
+WS_EPOCH, WS_ARRIVALS, WS_ERROR = 0, 1, 2
+ERR_COLLECT_SPIN = 0x1
+ERR_SPLITK_SPIN = 0x2
+
+
+class MxgError(Exception):
+    """A non-zero return code of the library."""
+
+    def __init__(self, code: int, what: str) -> None:
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+class MxgValueError(MxgError, ValueError):
+    """The arguments were rejected on the host; nothing was enqueued."""
+
+
+class MxgUnsupported(MxgValueError):
+    """Valid arguments that no kernel variant takes: the caller falls back."""
+
+
+class MxgHipError(MxgError, RuntimeError):
+    """A HIP call failed."""
+
+
+class mxg_mailbox(ctypes.Structure):
+    _fields_ = [
+        ("slots", ctypes.c_void_p),
+        ("state", ctypes.c_void_p),
+        ("ranks", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("capacity_bytes", ctypes.c_int64),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m mxfp8_decode_gemm_amd.build` "
+            "(there is no fallback implementation)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, u32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                             ctypes.c_size_t, ctypes.c_uint32)
+    mbp = ctypes.POINTER(mxg_mailbox)
+    sig = {
+        "mxg_mailbox_slots_bytes": (sz, [i32, i64]),
+        "mailbox_init": (ctypes.c_int, [mbp, vp, vp, i32, i32, i64, vp]),
+        "mxgemm_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "mxgemm_workspace_init": (ctypes.c_int, [vp, sz, vp]),
+        "mxgemm_publish": (ctypes.c_int, [mbp, vp, vp, vp, vp, i32, i32, i32, i32, vp, sz,
+                                          vp, vp]),
+        "mxgemm_publish_timed": (ctypes.c_int, [mbp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                                sz, vp, vp, vp, vp]),
+        "mailbox_publish": (ctypes.c_int, [mbp, i32, vp, i64, vp]),
+        "mailbox_collect": (ctypes.c_int, [mbp, vp, i64, vp]),
+        "mxg_set_spin_limit": (u32, [u32]),
+        "mxg_graph_begin": (ctypes.c_int, [vp]),
+        "mxg_graph_end": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
+        "mxg_graph_launch": (ctypes.c_int, [vp, vp]),
+        "mxg_graph_destroy": (ctypes.c_int, [vp]),
+        "mxg_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/mxgemm.h declares."""
+    with open(HEADER_PATH) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text,
+                       flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+
+def _ptr(obj) -> int | None:
+    if obj is None:
+        return None
+    if isinstance(obj, int):
+        return obj
+    dp = getattr(obj, "data_ptr", None)
+    if dp is None:
+        raise TypeError(f"expected a device tensor or address, got {type(obj).__name__}")
+    return int(dp())
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _event(ev) -> int | None:
+    if ev is None or isinstance(ev, int):
+        return ev
+    return int(ev.cuda_event)
+
+
+def _check(code: int, what: str) -> None:
+    if code == OK:
+        return
+    if code == EUNSUPPORTED:
+        raise MxgUnsupported(code, what)
+    if code == EHIP:
+        raise MxgHipError(code, what)
+    raise MxgValueError(code, what)
+
+
+def strerror(code: int) -> str:
+    return _lib.mxg_strerror(code).decode()
+
+
+# ---------------------------------------------------------------------------
+# the C ABI, same names
+# ---------------------------------------------------------------------------
+
+
+def mxg_mailbox_slots_bytes(ranks: int, capacity_bytes: int) -> int:
+    return int(_lib.mxg_mailbox_slots_bytes(ranks, capacity_bytes))
+
+
+def mailbox_init(slots, state, ranks: int, rank: int, capacity_bytes: int,
+                 stream=None) -> mxg_mailbox:
+    mb = mxg_mailbox()
+    _check(_lib.mailbox_init(ctypes.byref(mb), _ptr(slots), _ptr(state), ranks, rank,
+                             capacity_bytes, _stream(stream)), "mailbox_init")
+    return mb
+
+
+def mxgemm_workspace_bytes(m: int, n: int, k: int, split_k: int) -> int:
+    return int(_lib.mxgemm_workspace_bytes(m, n, k, split_k))
+
+
+def mxgemm_workspace_init(workspace, workspace_bytes: int, stream=None) -> None:
+    _check(_lib.mxgemm_workspace_init(_ptr(workspace), workspace_bytes, _stream(stream)),
+           "mxgemm_workspace_init")
+
+
+def mxgemm_publish(mb: mxg_mailbox, w, w_scale, x, x_scale, m: int, n: int, k: int,
+                   split_k: int = 1, workspace=None, workspace_bytes: int = 0,
+                   c_out=None, stream=None) -> None:
+    _check(_lib.mxgemm_publish(ctypes.byref(mb), _ptr(w), _ptr(w_scale), _ptr(x),
+                               _ptr(x_scale), m, n, k, split_k, _ptr(workspace),
+                               workspace_bytes, _ptr(c_out), _stream(stream)),
+           "mxgemm_publish")
+
+
+def mxgemm_publish_timed(mb: mxg_mailbox, w, w_scale, x, x_scale, m: int, n: int, k: int,
+                         split_k: int, workspace, workspace_bytes: int, c_out, stream,
+                         ev_start, ev_stop) -> None:
+    """mxgemm_publish with HIP events recorded around the kernel itself;
+    events are torch.cuda.Event objects (their cuda_event handle is passed)
+    or raw hipEvent_t integers."""
+    _check(_lib.mxgemm_publish_timed(ctypes.byref(mb), _ptr(w), _ptr(w_scale), _ptr(x),
+                                     _ptr(x_scale), m, n, k, split_k, _ptr(workspace),
+                                     workspace_bytes, _ptr(c_out), _stream(stream),
+                                     _event(ev_start), _event(ev_stop)),
+           "mxgemm_publish_timed")
+
+
+def mailbox_publish(mb: mxg_mailbox, rank: int, src, nbytes: int, stream=None) -> None:
+    _check(_lib.mailbox_publish(ctypes.byref(mb), rank, _ptr(src), nbytes, _stream(stream)),
+           "mailbox_publish")
+
+
+def mailbox_collect(mb: mxg_mailbox, out, nbytes: int, stream=None) -> None:
+    _check(_lib.mailbox_collect(ctypes.byref(mb), _ptr(out), nbytes, _stream(stream)),
+           "mailbox_collect")
+
+
+def mxg_set_spin_limit(polls: int) -> int:
+    return int(_lib.mxg_set_spin_limit(polls))
+
+
+def mxg_graph_begin(stream=None) -> None:
+    _check(_lib.mxg_graph_begin(_stream(stream)), "mxg_graph_begin")
+
+
+def mxg_graph_end(stream=None) -> int:
+    exec_ = ctypes.c_void_p()
+    _check(_lib.mxg_graph_end(_stream(stream), ctypes.byref(exec_)), "mxg_graph_end")
+    return int(exec_.value)
+
+
+def mxg_graph_launch(exec_: int, stream=None) -> None:
+    _check(_lib.mxg_graph_launch(exec_, _stream(stream)), "mxg_graph_launch")
+
+
+def mxg_graph_destroy(exec_: int) -> None:
+    _check(_lib.mxg_graph_destroy(exec_), "mxg_graph_destroy")
+
+
+def mxg_strerror(code: int) -> str:
+    return strerror(code)

@@ -1,0 +1,214 @@
+// C ABI of the MXFP8 publishing GEMM library: host-side validation (from
+// sizes and addresses only, before any HIP call), dispatch, graph helpers.
+// The declarations, argument meanings and error rules are in
+// include/mxgemm.h.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "../../include/mxgemm.h"
+#include "mxgemm_internal.h"
+
+namespace mxg {
+namespace {
+std::atomic<uint32_t> g_spin_limit{1u << 20};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool mailbox_ok(const mxg_mailbox* mb) {
+  return mb && mb->slots && mb->state && mb->ranks >= 1 && mb->ranks <= MXG_MAX_RANKS &&
+         mb->rank >= 0 && mb->rank < mb->ranks && mb->capacity_bytes > 0 &&
+         mb->capacity_bytes % MXG_PACK_BYTES == 0;
+}
+
+int hip_code(hipError_t e) { return e == hipSuccess ? MXG_OK : MXG_EHIP; }
+}  // namespace
+
+uint32_t spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+}  // namespace mxg
+
+using namespace mxg;
+
+extern "C" {
+
+size_t mxg_mailbox_slots_bytes(int32_t ranks, int64_t capacity_bytes) {
+  if (ranks < 1 || ranks > MXG_MAX_RANKS || capacity_bytes <= 0 ||
+      capacity_bytes % MXG_PACK_BYTES)
+    return 0;
+  return (size_t)MXG_GENERATIONS * (size_t)ranks * (size_t)capacity_bytes;
+}
+
+int mailbox_init(mxg_mailbox* mb, void* slots, uint32_t* state, int32_t ranks, int32_t rank,
+                 int64_t capacity_bytes, void* stream) {
+  if (!mb || !slots || !state) return MXG_EINVAL;
+  const size_t bytes = mxg_mailbox_slots_bytes(ranks, capacity_bytes);
+  if (bytes == 0 || rank < 0 || rank >= ranks) return MXG_EINVAL;
+  if (!aligned16(slots) || !aligned16(state)) return MXG_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_fill_u32(static_cast<uint32_t*>(slots), bytes / 4, MXG_SENTINEL, s);
+  if (e == hipSuccess) e = launch_state_init(state, s);
+  if (e != hipSuccess) return MXG_EHIP;
+  mb->slots = slots;
+  mb->state = state;
+  mb->ranks = ranks;
+  mb->rank = rank;
+  mb->capacity_bytes = capacity_bytes;
+  return MXG_OK;
+}
+
+size_t mxgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t split_k) {
+  (void)m;
+  (void)k;
+  if (split_k <= 1 || n <= 0) return 0;
+  const size_t n8 = (size_t)((n + 7) / 8) * 8;
+  // pairs[split][token 0..7][n / 8][8] of 8 bytes
+  return MXG_WS_HEADER_BYTES + (size_t)split_k * 8 * n8 * 8;
+}
+
+int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < MXG_WS_HEADER_BYTES || workspace_bytes % 16)
+    return MXG_EINVAL;
+  if (!aligned16(workspace)) return MXG_EALIGN;
+  return hip_code(launch_workspace_init(static_cast<uint32_t*>(workspace), workspace_bytes,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+int publish_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                 const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n, int32_t k,
+                 int32_t split_k, void* workspace, size_t workspace_bytes, uint16_t* c_out,
+                 void* stream, void* ev_start, void* ev_stop) {
+  if (!mailbox_ok(mb) || !w || !w_scale || !x || !x_scale) return MXG_EINVAL;
+  if (m < 1 || m > MXG_MAX_ROWS || n <= 0 || n % 8 || k <= 0 || k % 128) return MXG_EINVAL;
+  if (split_k != 1 && split_k != 2 && split_k != 4 && split_k != 8) return MXG_EINVAL;
+  if (k % (128 * split_k)) return MXG_EINVAL;
+  if (!aligned16(w) || !aligned16(w_scale) || !aligned16(x) || !aligned16(x_scale) ||
+      !aligned16(mb->slots) || !aligned16(mb->state) || (c_out && !aligned16(c_out)))
+    return MXG_EALIGN;
+  if ((int64_t)2 * m * n > mb->capacity_bytes) return MXG_ECAPACITY;
+  if (split_k > 1) {
+    if (!workspace || workspace_bytes < mxgemm_workspace_bytes(m, n, k, split_k))
+      return MXG_EWORKSPACE;
+    if (!aligned16(workspace)) return MXG_EALIGN;
+  }
+  // The tile choice also checks that a split-K grid can be resident at once:
+  // the workgroups of one output tile wait for each other's partials.
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MXG_EHIP;
+  TileCfg cfg;
+  if (!choose_tile(m, n, k, split_k, &cfg)) return MXG_EUNSUPPORTED;
+
+  GemmArgs a;
+  a.w = w;
+  a.ws = w_scale;
+  a.x = x;
+  a.xs = x_scale;
+  a.slot = static_cast<uint8_t*>(mb->slots) + (size_t)mb->rank * mb->capacity_bytes;
+  a.gen_stride = (int64_t)mb->ranks * mb->capacity_bytes;
+  a.state = mb->state;
+  a.ws_hdr = split_k > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.pairs = split_k > 1 ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
+                                                       MXG_WS_HEADER_BYTES)
+                        : nullptr;
+  a.c_out = c_out;
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  a.split_k = split_k;
+  a.spin_limit = spin_limit();
+  return hip_code(launch_gemm_publish(a, cfg, static_cast<hipStream_t>(stream),
+                                      static_cast<hipEvent_t>(ev_start),
+                                      static_cast<hipEvent_t>(ev_stop)));
+}
+}  // namespace
+
+int mxgemm_publish(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                   const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n, int32_t k,
+                   int32_t split_k, void* workspace, size_t workspace_bytes, uint16_t* c_out,
+                   void* stream) {
+  return publish_impl(mb, w, w_scale, x, x_scale, m, n, k, split_k, workspace, workspace_bytes,
+                      c_out, stream, nullptr, nullptr);
+}
+
+int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                         const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n,
+                         int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
+                         uint16_t* c_out, void* stream, void* ev_start, void* ev_stop) {
+  if (!ev_start || !ev_stop) return MXG_EINVAL;
+  return publish_impl(mb, w, w_scale, x, x_scale, m, n, k, split_k, workspace, workspace_bytes,
+                      c_out, stream, ev_start, ev_stop);
+}
+
+int mailbox_publish(const mxg_mailbox* mb, int32_t rank, const void* src, int64_t nbytes,
+                    void* stream) {
+  if (!mailbox_ok(mb) || !src || rank < 0 || rank >= mb->ranks) return MXG_EINVAL;
+  if (!aligned16(src) || !aligned16(mb->slots) || !aligned16(mb->state)) return MXG_EALIGN;
+  if (nbytes <= 0 || nbytes > mb->capacity_bytes || nbytes % MXG_PACK_BYTES)
+    return MXG_ECAPACITY;
+  uint8_t* slot = static_cast<uint8_t*>(mb->slots) + (size_t)rank * mb->capacity_bytes;
+  return hip_code(launch_mailbox_publish(slot, (int64_t)mb->ranks * mb->capacity_bytes,
+                                         mb->state, static_cast<const uint8_t*>(src), nbytes,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream) {
+  if (!mailbox_ok(mb) || !out) return MXG_EINVAL;
+  if (!aligned16(out) || !aligned16(mb->slots) || !aligned16(mb->state)) return MXG_EALIGN;
+  if (nbytes <= 0 || nbytes > mb->capacity_bytes || nbytes % MXG_PACK_BYTES)
+    return MXG_ECAPACITY;
+  return hip_code(launch_mailbox_collect(
+      static_cast<uint8_t*>(mb->slots), (int64_t)mb->ranks * mb->capacity_bytes,
+      mb->capacity_bytes, mb->ranks, mb->state, static_cast<uint8_t*>(out), nbytes,
+      spin_limit(), static_cast<hipStream_t>(stream)));
+}
+
+uint32_t mxg_set_spin_limit(uint32_t polls) {
+  return g_spin_limit.exchange(polls == 0 ? (1u << 20) : polls);
+}
+
+int mxg_graph_begin(void* stream) {
+  if (!stream) return MXG_EINVAL;  // the null stream cannot be captured
+  return hip_code(
+      hipStreamBeginCapture(static_cast<hipStream_t>(stream), hipStreamCaptureModeRelaxed));
+}
+
+int mxg_graph_end(void* stream, void** exec) {
+  if (!stream || !exec) return MXG_EINVAL;
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(static_cast<hipStream_t>(stream), &graph);
+  if (e != hipSuccess) return MXG_EHIP;
+  hipGraphExec_t ge = nullptr;
+  e = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (e != hipSuccess) return MXG_EHIP;
+  *exec = ge;
+  return MXG_OK;
+}
+
+int mxg_graph_launch(void* exec, void* stream) {
+  if (!exec) return MXG_EINVAL;
+  return hip_code(
+      hipGraphLaunch(static_cast<hipGraphExec_t>(exec), static_cast<hipStream_t>(stream)));
+}
+
+int mxg_graph_destroy(void* exec) {
+  if (!exec) return MXG_EINVAL;
+  return hip_code(hipGraphExecDestroy(static_cast<hipGraphExec_t>(exec)));
+}
+
+const char* mxg_strerror(int code) {
+  switch (code) {
+    case MXG_OK: return "ok";
+    case MXG_EINVAL: return "invalid argument (null pointer, shape, rank or split_k)";
+    case MXG_EALIGN: return "pointer not 16-byte aligned";
+    case MXG_ECAPACITY: return "payload does not fit the mailbox slot";
+    case MXG_EWORKSPACE: return "split-K workspace missing or too small";
+    case MXG_EUNSUPPORTED: return "no kernel variant for these sizes on this device";
+    case MXG_EHIP: return "HIP error";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

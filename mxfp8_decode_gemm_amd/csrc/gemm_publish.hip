@@ -1,0 +1,584 @@
+// The low-batch MXFP8 GEMM with the Lamport publish in its epilogue, for
+// gfx950 (MI355X).
+//
+// What it computes (publishing_gemm page = the API page of
+// vllm.models.deepseek_v41.nvidia.specialized_decode.boundary.publishing_gemm;
+// module docstring, "GEMM structure", and epilog_warp / publish_value):
+//   C[t, n] = sum_k W[n, k] x[t, k] over e4m3fn data with one E8M0 scale per
+//   32 K, FP32 accumulation, split-K over `split_k` workgroups that exchange
+//   FP32 partials and each reduce a share of the tile, then BF16 rounding,
+//   negative-zero clearing and one 16-byte store per eight consecutive
+//   columns of one token into the mailbox slot of generation state[NEXT].
+//
+// How it is laid out on CDNA4 (not the pages' Blackwell design):
+//   * Numerics. W is the MFMA A operand (16 output rows per instruction), x
+//     the B operand (16 token columns; tokens >= m are zero). Each e4m3 byte
+//     is turned, with its E8M0 scale, into the exact BF16 value
+//     dec(byte) * 2^(scale-127) by v_cvt_scalef32_pk_bf16_fp8, and the
+//     contraction runs on v_mfma_f32_16x16x32_bf16 with FP32 accumulation.
+//     gfx950's scaled fp8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4) was
+//     measured on the device to drop the low bits of every product smaller
+//     than about 2^-13 of the largest product in its 32-element scale block,
+//     a biased truncation that grows with K and breaks the 1 BF16 ulp +
+//     1e-6 sum|W x| acceptance bound; the BF16 instruction keeps products to
+//     about 2^-25 of the largest in its 32-element K step. The path is HBM
+//     bound, so the 4x MFMA count and the conversions cost well under a tenth
+//     of the kernel's time.
+//   * W never touches LDS: each lane streams its two 16-byte pieces of every
+//     128-wide K block straight from HBM into VGPRs (one instruction reads 64
+//     contiguous bytes of each of 16 rows), `depth` K blocks ahead. Lane l
+//     holds row l % 16 and K = 16*(l/16) + 0..15 and 64 + 16*(l/16) + 0..15
+//     of the block; the BF16 MFMA pairs A and B elements by lane group and
+//     position (measured), so the B operand uses the same K split.
+//   * x and its scales for the workgroup's K slice are staged once in LDS, in
+//     the order the B operand reads them, and shared by every wave.
+//   * The waves of a workgroup split its K slice; their partial tiles meet in
+//     LDS and are summed in ascending K order.
+//   * Split-K across workgroups: every tile pack (8 columns of one token) has
+//     one owner slice (pack index mod split_k). The other slices store their
+//     partial pack as eight (FP32 bits, epoch) 64-bit pairs with agent-scope
+//     stores; the owner polls all of its pairs in one batch until every tag
+//     equals this launch's epoch (sync page = vllm.models.deepseek_v41.amd.
+//     mono.common.sync, Mailbox: one round trip, no drain, no flag), then
+//     sums the slices in ascending K order.
+//   * One thread owns one pack, so the eight BF16 values leave as one aligned
+//     16-byte store, with no cross-lane shuffle.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "../../include/mxgemm.h"
+#include "mxgemm_internal.h"
+
+namespace mxg {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// 2^(s-127) as an FP32 multiplier: the biased exponent s in the exponent
+// field; s == 0 is the subnormal 2^-127.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+
+// Eight e4m3fn bytes (two dwords, lowest byte first) times a power-of-two
+// scale, as eight BF16 values. v_cvt_scalef32_pk_bf16_fp8 converts two bytes
+// of a dword per instruction; an e4m3 value times 2^k is exact in BF16 for
+// every scale the workloads use, and the instruction rounds to nearest even.
+__device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1, float scale) {
+  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
+  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
+  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false);
+  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
+  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+constexpr int kHeaderBytes = 16;  // LDS: [0] generation, [1] epoch
+
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// BF16 bits of an FP32 value, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Each BF16 half equal to 0x8000 (negative zero) becomes 0x0000.
+__device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
+  const uint32_t lo = (w & 0xFFFFu) == 0x8000u ? 0u : (w & 0xFFFFu);
+  const uint32_t hi = (w >> 16) == 0x8000u ? 0u : (w & 0xFFFF0000u);
+  return lo | hi;
+}
+
+// Sum of the wave partials of pack (t, jc) in ascending K order: the waves
+// of a workgroup cover its K slice in order wk = 0, 1, ...
+template <int WK>
+__device__ __forceinline__ void wave_sum(const float* red, int m, int ntile, int t, int jc,
+                                         float v[8]) {
+  const float* src = red + (size_t)t * ntile + 8 * jc;
+  const v4f p0 = *reinterpret_cast<const v4f*>(src);
+  const v4f p1 = *reinterpret_cast<const v4f*>(src + 4);
+  v[0] = p0[0]; v[1] = p0[1]; v[2] = p0[2]; v[3] = p0[3];
+  v[4] = p1[0]; v[5] = p1[1]; v[6] = p1[2]; v[7] = p1[3];
+#pragma unroll
+  for (int w = 1; w < WK; ++w) {
+    const float* s2 = red + (size_t)(w * m + t) * ntile + 8 * jc;
+    const v4f q0 = *reinterpret_cast<const v4f*>(s2);
+    const v4f q1 = *reinterpret_cast<const v4f*>(s2 + 4);
+    v[0] += q0[0]; v[1] += q0[1]; v[2] += q0[2]; v[3] += q0[3];
+    v[4] += q1[0]; v[5] += q1[1]; v[6] += q1[2]; v[7] += q1[3];
+  }
+}
+
+// Copies x chunks (16 bytes) of the workgroup's K slice into LDS in the order
+// the MFMA B operand reads them: chunk (kb, half, group, t) holds
+// x[t][kb*128 + 64*half + 16*group .. +16).
+template <int NT>
+struct XStage {
+  static constexpr int kChunks = 4;  // chunks per thread per round
+  uint4 v0, v1, v2, v3;
+  int d0, d1, d2, d3;
+
+  __device__ __forceinline__ static int dest(int c, int cpr, int m) {
+    const int t = c / cpr;
+    const int q = c - t * cpr;
+    const int kb = q >> 3, w8 = q & 7;
+    return ((kb * 2 + (w8 >> 2)) * 4 + (w8 & 3)) * m + t;
+  }
+  __device__ __forceinline__ static uint4 src(const uint8_t* x, int K, size_t k0, int c, int cpr) {
+    const int t = c / cpr;
+    const int q = c - t * cpr;
+    return *reinterpret_cast<const uint4*>(x + (size_t)t * K + k0 + 16 * q);
+  }
+  __device__ __forceinline__ void load(const uint8_t* x, int K, size_t k0, int m, int cpr,
+                                       int xch, int c0, int tid) {
+    const uint4 z = {0u, 0u, 0u, 0u};
+    const int c_0 = c0 + tid, c_1 = c0 + NT + tid, c_2 = c0 + 2 * NT + tid, c_3 = c0 + 3 * NT + tid;
+    v0 = c_0 < xch ? src(x, K, k0, c_0, cpr) : z;
+    v1 = c_1 < xch ? src(x, K, k0, c_1, cpr) : z;
+    v2 = c_2 < xch ? src(x, K, k0, c_2, cpr) : z;
+    v3 = c_3 < xch ? src(x, K, k0, c_3, cpr) : z;
+    d0 = c_0 < xch ? dest(c_0, cpr, m) : -1;
+    d1 = c_1 < xch ? dest(c_1, cpr, m) : -1;
+    d2 = c_2 < xch ? dest(c_2, cpr, m) : -1;
+    d3 = c_3 < xch ? dest(c_3, cpr, m) : -1;
+  }
+  __device__ __forceinline__ void store(uint4* xl) const {
+    if (d0 >= 0) xl[d0] = v0;
+    if (d1 >= 0) xl[d1] = v1;
+    if (d2 >= 0) xl[d2] = v2;
+    if (d3 >= 0) xl[d3] = v3;
+  }
+};
+
+template <int RB, int WN, int WK, int D, int SK>
+__global__ void __launch_bounds__(64 * WN * WK)
+gemm_publish_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int NT = 64 * WN * WK;
+  constexpr int RBT = RB * WN;    // 16-row blocks per tile
+  constexpr int NTILE = 16 * RBT; // rows per tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wn = wave % WN;
+  const int wk = wave / WN;
+  const int r16 = lane & 15;  // A row / B column of this lane
+  const int grp = lane >> 4;  // lane group: K pieces and scale block
+
+  constexpr int S = SK;  // split-K slices (the launch's split_k)
+  const int tile = blockIdx.x / S;
+  const int slice = blockIdx.x - tile * S;
+  const int m = a.m, N = a.n, K = a.k;
+  const int KS = K / S;             // K slice of this workgroup
+  const int NB = KS >> 7;           // 128-wide K blocks in the slice
+  const int kb_lo = (wk * NB) / WK; // this wave's K blocks
+  const int kb_hi = ((wk + 1) * NB) / WK;
+  const int nbw = kb_hi - kb_lo;
+  const int row0 = tile * NTILE;
+  const size_t kslice0 = (size_t)slice * KS;
+
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(lds);
+  uint4* xl = reinterpret_cast<uint4*>(lds + kHeaderBytes);
+  uint8_t* xsl = lds + kHeaderBytes + (size_t)m * KS;
+
+  // ---- call hand-off: generation and epoch, read before arriving --------
+  // (all_gather page, _AllGatherKernel.kernel: each CTA reads the state once
+  // before it counts itself; the last CTA advances it.)
+  uint32_t gen = 0, epoch = 0, arrived = 0;
+  if (tid == 0) {
+    gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
+    if (S > 1) {
+      epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH);
+      arrived = __hip_atomic_fetch_add(a.ws_hdr + MXG_WS_ARRIVALS, 1u, __ATOMIC_ACQ_REL,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // ---- x slice -> LDS, first round (loads issued before the W stream) ----
+  const int cpr = KS >> 4;  // 16-byte chunks per x row in the slice
+  const int xch = m * cpr;
+  XStage<NT> xst;
+  xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
+
+  // ---- W stream prologue -------------------------------------------------
+  const uint8_t* wrow[RB];
+  const uint32_t* wsrow[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    int row = row0 + (wn * RB + i) * 16 + r16;
+    row = row < N ? row : N - 1;  // rows past N load row N-1; never published
+    wrow[i] = a.w + (size_t)row * K + kslice0 + 16 * grp;
+    wsrow[i] = reinterpret_cast<const uint32_t*>(a.ws + (size_t)row * (K >> 5) + (kslice0 >> 5));
+  }
+  uint4 wlo[D][RB], whi[D][RB];
+  uint32_t wsc[D][RB];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (d < nbw) {
+      const int kb = kb_lo + d;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        wlo[d][i] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)kb * 128);
+        whi[d][i] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)kb * 128 + 64);
+        wsc[d][i] = wsrow[i][kb];
+      }
+    }
+  }
+
+  // ---- finish staging x and its scales ----------------------------------
+  xst.store(xl);
+  for (int c0 = XStage<NT>::kChunks * NT; c0 < xch; c0 += XStage<NT>::kChunks * NT) {
+    xst.load(a.x, K, kslice0, m, cpr, xch, c0, tid);
+    xst.store(xl);
+  }
+  {
+    const int wpr = KS >> 7;  // scale dwords per x row in the slice
+    const int nw = m * wpr;
+    for (int c = tid; c < nw; c += NT) {
+      const int t = c / wpr;
+      const int q = c - t * wpr;
+      reinterpret_cast<uint32_t*>(xsl)[c] =
+          *reinterpret_cast<const uint32_t*>(a.xs + (size_t)t * (K >> 5) + (kslice0 >> 5) + 4 * q);
+    }
+  }
+  if (tid == 0) {
+    hdr[0] = gen;
+    hdr[1] = epoch;
+    if (S > 1 && arrived == gridDim.x - 1u) {
+      // Last workgroup of this launch to arrive: every workgroup has read the
+      // epoch, so the next launch may use the next one (never 0).
+      const uint32_t next = epoch + 1u == 0u ? 1u : epoch + 1u;
+      st_agent_u32(a.ws_hdr + MXG_WS_ARRIVALS, 0u);
+      st_agent_u32(a.ws_hdr + MXG_WS_EPOCH, next);
+    }
+  }
+  __syncthreads();
+
+  // ---- main loop: K blocks of this wave ---------------------------------
+  v4f acc[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  const bool tok = r16 < m;
+  const int kspw = KS >> 5;  // scale bytes per x row in the slice
+  const int sb0 = grp >> 1;  // 32-block of this lane's first 16 K (its second is sb0 + 2)
+  for (int base = 0; base < nbw; base += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int j = base + d;
+      if (j < nbw) {
+        const int kb = kb_lo + j;
+        // B operand: x of this lane's token, as exact BF16, four K steps.
+        v8bf bx[4];
+        if (tok) {
+          const uint4 xlo = xl[((kb * 2 + 0) * 4 + grp) * m + r16];
+          const uint4 xhi = xl[((kb * 2 + 1) * 4 + grp) * m + r16];
+          const uint8_t* xsr = xsl + r16 * kspw + kb * 4;
+          const float fs0 = e8m0_to_f32(xsr[sb0]);
+          const float fs1 = e8m0_to_f32(xsr[sb0 + 2]);
+          bx[0] = fp8x8_to_bf16(xlo.x, xlo.y, fs0);
+          bx[1] = fp8x8_to_bf16(xlo.z, xlo.w, fs0);
+          bx[2] = fp8x8_to_bf16(xhi.x, xhi.y, fs1);
+          bx[3] = fp8x8_to_bf16(xhi.z, xhi.w, fs1);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bx[q] = v8bf{};
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const float fa0 = e8m0_to_f32((wsc[d][i] >> (8 * sb0)) & 0xFFu);
+          const float fa1 = e8m0_to_f32((wsc[d][i] >> (8 * (sb0 + 2))) & 0xFFu);
+          const v8bf a0 = fp8x8_to_bf16(wlo[d][i].x, wlo[d][i].y, fa0);
+          const v8bf a1 = fp8x8_to_bf16(wlo[d][i].z, wlo[d][i].w, fa0);
+          const v8bf a2 = fp8x8_to_bf16(whi[d][i].x, whi[d][i].y, fa1);
+          const v8bf a3 = fp8x8_to_bf16(whi[d][i].z, whi[d][i].w, fa1);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bx[0], acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bx[1], acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bx[2], acc[i], 0, 0, 0);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, bx[3], acc[i], 0, 0, 0);
+        }
+        if (j + D < nbw) {
+          const int kn = kb + D;
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            wlo[d][i] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)kn * 128);
+            whi[d][i] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)kn * 128 + 64);
+            wsc[d][i] = wsrow[i][kn];
+          }
+        }
+      }
+    }
+  }
+
+  // ---- partial tile -> LDS [wk][t][row], summed over waves in K order ---
+  __syncthreads();  // every wave is done with x in LDS
+  float* red = reinterpret_cast<float*>(lds + kHeaderBytes);
+  if (tok) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int rl = (wn * RB + i) * 16 + 4 * grp;
+      *reinterpret_cast<v4f*>(red + ((size_t)(wk * m + r16) * NTILE + rl)) = acc[i];
+    }
+  }
+  __syncthreads();
+  gen = hdr[0];
+  epoch = hdr[1];
+
+  // ---- one thread per pack: split-K exchange, BF16, publish -------------
+  constexpr int PPR = NTILE / 8;  // packs per token row of the tile
+  const int npacks = m * PPR;
+  uint8_t* slot = a.slot + (size_t)gen * a.gen_stride;
+  const size_t ncols = (size_t)(N >> 3);
+  // Pass 1 (split-K only): store the partial packs other slices own. Every
+  // send is issued before this thread polls anything, so no two workgroups
+  // can wait on each other.
+  if (SK > 1) {
+    for (int P = tid; P < npacks; P += NT) {
+      const int t = P / PPR;
+      const int jc = P - t * PPR;
+      const int n0 = row0 + 8 * jc;
+      if (n0 >= N || P % SK == slice) continue;
+      float v[8];
+      wave_sum<WK>(red, m, NTILE, t, jc, v);
+      // pairs[(slice * 8 + t) * (N / 8) + n / 8][0..7]
+      uint64_t* dst = a.pairs + (((size_t)slice * 8 + t) * ncols + (n0 >> 3)) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        st_agent_u64(dst + e, (uint64_t)__float_as_uint(v[e]) | ((uint64_t)epoch << 32));
+    }
+  }
+  // Pass 2: the packs this slice owns (all of them without split-K).
+  for (int P = tid; P < npacks; P += NT) {
+    const int t = P / PPR;
+    const int jc = P - t * PPR;
+    const int n0 = row0 + 8 * jc;
+    if (n0 >= N || (SK > 1 && P % SK != slice)) continue;
+    float v[8];
+    wave_sum<WK>(red, m, NTILE, t, jc, v);
+    if (SK > 1) {
+      // Poll the other slices' pairs of this pack in one batch.
+      uint64_t pv[SK > 1 ? SK - 1 : 1][8];
+      uint32_t polls = 0;
+      for (;;) {
+#pragma unroll
+        for (int o = 0; o < SK - 1; ++o) {
+          const int src = o < slice ? o : o + 1;
+          const uint64_t* p = a.pairs + (((size_t)src * 8 + t) * ncols + (n0 >> 3)) * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[o][e] = ld_agent_u64(p + e);
+        }
+        bool pending = false;
+#pragma unroll
+        for (int o = 0; o < SK - 1; ++o)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pending |= (uint32_t)(pv[o][e] >> 32) != epoch;
+        if (!pending) break;
+        if (++polls >= a.spin_limit) {
+          __hip_atomic_fetch_or(a.ws_hdr + MXG_WS_ERROR, MXG_ERR_SPLITK_SPIN, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      // Sum the slices in ascending K order, this slice's partial in place:
+      // slot o of pv holds slice o for o < slice and slice o + 1 above it.
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = slice == 0 ? v[e] : __uint_as_float((uint32_t)pv[0][e]);
+#pragma unroll
+      for (int o = 1; o < SK; ++o) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float term;
+          if (o == slice) {
+            term = v[e];
+          } else if (o < slice) {
+            term = __uint_as_float((uint32_t)pv[o][e]);
+          } else {
+            term = __uint_as_float((uint32_t)pv[o - 1][e]);
+          }
+          r[e] += term;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = r[e];
+    }
+    // BF16 (nearest even), raw store, negative-zero clear, 16-byte publish.
+    uint4 raw;
+    raw.x = bf16_pair(v[0], v[1]);
+    raw.y = bf16_pair(v[2], v[3]);
+    raw.z = bf16_pair(v[4], v[5]);
+    raw.w = bf16_pair(v[6], v[7]);
+    const size_t off = ((size_t)t * N + n0) * 2;
+    if (a.c_out) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.c_out) + off) = raw;
+    uint4 clean;
+    clean.x = clear_negative_zero(raw.x);
+    clean.y = clear_negative_zero(raw.y);
+    clean.z = clear_negative_zero(raw.z);
+    clean.w = clear_negative_zero(raw.w);
+    *reinterpret_cast<uint4*>(slot + off) = clean;
+  }
+
+  // Hand the generation to the consumer once per grid (publishing_gemm page,
+  // epilog_warp: block 0, one thread, sets the active stage word).
+  if (blockIdx.x == 0 && tid == 0) st_agent_u32(a.state + MXG_STATE_ACTIVE, gen);
+}
+
+// ---- variant table --------------------------------------------------------
+struct Variant {
+  TileCfg cfg;
+  int split_k;
+  const void* fn;
+};
+
+#define MXG_V(RB, WN, WK, D, SK) \
+  Variant{TileCfg{RB, WN, WK, D}, SK, \
+          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK>)}
+#define MXG_VARIANT(RB, WN, WK, D) \
+  MXG_V(RB, WN, WK, D, 1), MXG_V(RB, WN, WK, D, 2), MXG_V(RB, WN, WK, D, 4), \
+      MXG_V(RB, WN, WK, D, 8)
+
+const Variant kVariants[] = {
+    MXG_VARIANT(1, 1, 4, 4),  MXG_VARIANT(1, 1, 8, 4),  MXG_VARIANT(1, 1, 16, 4),
+    MXG_VARIANT(1, 1, 8, 8),  MXG_VARIANT(2, 1, 4, 4),  MXG_VARIANT(2, 1, 8, 2),
+    MXG_VARIANT(1, 2, 4, 4),  MXG_VARIANT(4, 1, 4, 4),  MXG_VARIANT(7, 1, 8, 2),
+    MXG_VARIANT(1, 7, 2, 8),  MXG_VARIANT(2, 1, 4, 8),  MXG_VARIANT(1, 1, 4, 8),
+};
+
+const Variant* find_variant(const TileCfg& c, int split_k) {
+  for (const Variant& v : kVariants)
+    if (v.cfg.rb == c.rb && v.cfg.wn == c.wn && v.cfg.wk == c.wk && v.cfg.depth == c.depth &&
+        v.split_k == split_k)
+      return &v;
+  return nullptr;
+}
+
+}  // namespace
+
+size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice) {
+  const size_t xbytes = (size_t)m * k_slice + (size_t)m * (k_slice / 32);
+  const size_t red = (size_t)c.wk * m * tile_rows(c) * sizeof(float);
+  return kHeaderBytes + std::max(xbytes, red);
+}
+
+bool tile_available(const TileCfg& c) { return find_variant(c, 1) != nullptr; }
+
+bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
+  const int ks = k / split_k;
+  auto fits = [&](const TileCfg& c) {
+    if (!find_variant(c, split_k) || gemm_lds_bytes(c, m, ks) > 160 * 1024) return false;
+    if (split_k == 1) return true;
+    // The workgroups of one tile wait for each other: the grid must be
+    // resident all at once.
+    const long tiles = (n + tile_rows(c) - 1) / tile_rows(c);
+    const long resident = gemm_resident_blocks(c, split_k, gemm_lds_bytes(c, m, ks));
+    return resident > 0 && tiles * split_k <= resident;
+  };
+  if (const char* env = std::getenv("MXG_TILE")) {
+    // Measurement override: exactly this variant, or no launch at all.
+    TileCfg c{};
+    if (std::sscanf(env, "%d,%d,%d,%d", &c.rb, &c.wn, &c.wk, &c.depth) != 4 || !fits(c))
+      return false;
+    *out = c;
+    return true;
+  }
+  // Preference order: enough waves per CU to keep tens of KB of W in flight,
+  // tiles wide enough to reuse the staged x, and (with split-K) a grid that
+  // is resident at once.
+  const int nb = ks / 128;
+  static const TileCfg kSplit[] = {{4, 1, 4, 4}, {7, 1, 8, 2}, {2, 1, 4, 4}, {1, 1, 4, 4},
+                                   {2, 1, 8, 2}, {1, 1, 8, 4}};
+  static const TileCfg kLongK[] = {{1, 1, 16, 4}, {1, 1, 8, 8}, {1, 1, 8, 4}, {1, 1, 4, 4}};
+  static const TileCfg kShortK[] = {{1, 1, 4, 4}, {1, 1, 8, 4}, {2, 1, 4, 4}};
+  const TileCfg* list;
+  size_t count;
+  if (split_k > 1) {
+    list = kSplit;
+    count = sizeof(kSplit) / sizeof(kSplit[0]);
+  } else if (nb >= 64) {
+    list = kLongK;
+    count = sizeof(kLongK) / sizeof(kLongK[0]);
+  } else {
+    list = kShortK;
+    count = sizeof(kShortK) / sizeof(kShortK[0]);
+  }
+  for (size_t i = 0; i < count; ++i) {
+    if (fits(list[i])) {
+      *out = list[i];
+      return true;
+    }
+  }
+  return false;
+}
+
+long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, int, size_t>, long> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const auto key = std::make_tuple(dev, c.rb, c.wn, c.wk * 100 + c.depth, split_k, lds_bytes);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  const Variant* v = find_variant(c, split_k);
+  if (!v) return -1;
+  int per_cu = 0, cus = 0;
+  if (lds_bytes > 64 * 1024 &&
+      hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+          hipSuccess)
+    return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->fn, tile_threads(c), lds_bytes) !=
+      hipSuccess)
+    return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  const long r = (long)per_cu * cus;
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = r;
+  return r;
+}
+
+hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t s,
+                               hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const Variant* v = find_variant(c, a.split_k);
+  if (!v) return hipErrorInvalidValue;
+  const int tiles = (a.n + tile_rows(c) - 1) / tile_rows(c);
+  const dim3 grid(tiles * a.split_k), block(tile_threads(c));
+  const size_t lds = gemm_lds_bytes(c, a.m, a.k / a.split_k);
+  if (lds > 64 * 1024) {
+    const hipError_t e =
+        hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  void* args[] = {const_cast<GemmArgs*>(&a)};
+  if (ev_start || ev_stop)
+    return hipExtLaunchKernel(v->fn, grid, block, args, lds, s, ev_start, ev_stop, 0);
+  return hipLaunchKernel(v->fn, grid, block, args, lds, s);
+}
+
+}  // namespace mxg

@@ -1,0 +1,186 @@
+// Mailbox kernels: arm, unfused publish and collect of the three-generation
+// Lamport mailbox, for gfx950.
+//
+// all_gather page = the API page of
+// vllm.models.deepseek_v41.nvidia.ops.cute_dsl.all_gather. Its module
+// docstring (steps 1-3) and _AllGatherKernel.kernel define the protocol this
+// file implements for emulated rank slots on one GPU:
+//   * idle words hold the sentinel 0x80000000;
+//   * a publish writes a rank's payload into its slot of the current
+//     generation (here with BF16 negative zero cleared, which also keeps the
+//     sentinel word out of every payload);
+//   * a collect polls each 16-byte pack of every rank's slot until none of
+//     its words is the sentinel, copies it out rank-major, stores the
+//     sentinel back, and the last workgroup to arrive advances the
+//     generation mod 3.
+// All payload traffic moves as 32-bit integers, never through float
+// registers (sync page, Mailbox.put_words: a NaN bit pattern would not
+// survive a float move).
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/mxgemm.h"
+#include "mxgemm_internal.h"
+
+namespace mxg {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr unsigned kMaxBlocks = 2048;
+
+__device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
+  const uint32_t lo = (w & 0xFFFFu) == 0x8000u ? 0u : (w & 0xFFFFu);
+  const uint32_t hi = (w >> 16) == 0x8000u ? 0u : (w & 0xFFFF0000u);
+  return lo | hi;
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t words, uint32_t value) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t quads = words / 4;
+  uint4* q = reinterpret_cast<uint4*>(p);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < quads; i += stride)
+    q[i] = uint4{value, value, value, value};
+  for (size_t i = quads * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride)
+    p[i] = value;
+}
+
+__global__ void state_init_kernel(uint32_t* state) {
+  const int i = threadIdx.x;
+  if (i < MXG_STATE_WORDS) state[i] = 0u;
+}
+
+__global__ void workspace_header_kernel(uint32_t* hdr) {
+  const int i = threadIdx.x;
+  if (i < MXG_WS_HEADER_BYTES / 4) hdr[i] = i == MXG_WS_EPOCH ? 1u : 0u;
+}
+
+// Unfused publish: one thread per 16-byte pack.
+__global__ void publish_kernel(uint8_t* slot, int64_t gen_stride, uint32_t* state,
+                               const uint8_t* src, int64_t packs) {
+  const uint32_t gen = ld_agent_u32(state + MXG_STATE_NEXT) % MXG_GENERATIONS;
+  uint4* dst = reinterpret_cast<uint4*>(slot + (size_t)gen * gen_stride);
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < packs; p += stride) {
+    uint4 v = s[p];
+    v.x = clear_negative_zero(v.x);
+    v.y = clear_negative_zero(v.y);
+    v.z = clear_negative_zero(v.z);
+    v.w = clear_negative_zero(v.w);
+    dst[p] = v;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) st_agent_u32(state + MXG_STATE_ACTIVE, gen);
+}
+
+// Collect: one thread per (rank, pack), grid-stride.
+__global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capacity, int ranks,
+                               uint32_t* state, uint8_t* out, int64_t nbytes,
+                               uint32_t spin_limit) {
+  __shared__ uint32_t shared_gen;
+  if (threadIdx.x == 0) {
+    // Read the generation once, then count this workgroup; the last one to
+    // arrive advances the generation (all_gather page, step 3).
+    const uint32_t g = ld_agent_u32(state + MXG_STATE_NEXT) % MXG_GENERATIONS;
+    shared_gen = g;
+    const uint32_t before = __hip_atomic_fetch_add(state + MXG_STATE_COLLECT_ARR, 1u,
+                                                   __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == gridDim.x - 1u) {
+      st_agent_u32(state + MXG_STATE_COLLECT_ARR, 0u);
+      st_agent_u32(state + MXG_STATE_NEXT, (g + 1u) % MXG_GENERATIONS);
+    }
+  }
+  __syncthreads();
+  const uint32_t gen = shared_gen;
+  const int64_t packs = nbytes / MXG_PACK_BYTES;
+  const int64_t total = packs * ranks;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint8_t* base = slots + (size_t)gen * gen_stride;
+  bool timed_out = false;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t r = i / packs;
+    const int64_t p = i - r * packs;
+    uint64_t* slot = reinterpret_cast<uint64_t*>(base + r * capacity + p * MXG_PACK_BYTES);
+    uint64_t lo, hi;
+    uint32_t polls = 0;
+    for (;;) {
+      lo = ld_agent_u64(slot);
+      hi = ld_agent_u64(slot + 1);
+      const bool dirty = (uint32_t)lo == MXG_SENTINEL || (uint32_t)(lo >> 32) == MXG_SENTINEL ||
+                         (uint32_t)hi == MXG_SENTINEL || (uint32_t)(hi >> 32) == MXG_SENTINEL;
+      if (!dirty) break;
+      if (++polls >= spin_limit) {
+        timed_out = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    uint4 v;
+    v.x = (uint32_t)lo;
+    v.y = (uint32_t)(lo >> 32);
+    v.z = (uint32_t)hi;
+    v.w = (uint32_t)(hi >> 32);
+    *reinterpret_cast<uint4*>(out + r * nbytes + p * MXG_PACK_BYTES) = v;
+    *reinterpret_cast<uint4*>(slot) =
+        uint4{MXG_SENTINEL, MXG_SENTINEL, MXG_SENTINEL, MXG_SENTINEL};
+  }
+  if (timed_out)
+    __hip_atomic_fetch_or(state + MXG_STATE_ERROR, MXG_ERR_COLLECT_SPIN, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+}
+
+unsigned blocks_for(int64_t items) {
+  const int64_t b = (items + kThreads - 1) / kThreads;
+  return (unsigned)(b < 1 ? 1 : (b > (int64_t)kMaxBlocks ? kMaxBlocks : b));
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s) {
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for((int64_t)(words / 4 + 1))), dim3(kThreads),
+                     0, s, p, words, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_init(uint32_t* state, hipStream_t s) {
+  hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(64), 0, s, state);
+  return hipGetLastError();
+}
+
+hipError_t launch_workspace_init(uint32_t* ws, size_t bytes, hipStream_t s) {
+  const size_t words = bytes / 4;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks_for((int64_t)(words / 4 + 1))), dim3(kThreads),
+                     0, s, ws, words, 0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(workspace_header_kernel, dim3(1), dim3(64), 0, s, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_mailbox_publish(uint8_t* slot, int64_t gen_stride, uint32_t* state,
+                                  const uint8_t* src, int64_t nbytes, hipStream_t s) {
+  const int64_t packs = nbytes / MXG_PACK_BYTES;
+  hipLaunchKernelGGL(publish_kernel, dim3(blocks_for(packs)), dim3(kThreads), 0, s, slot,
+                     gen_stride, state, src, packs);
+  return hipGetLastError();
+}
+
+hipError_t launch_mailbox_collect(uint8_t* slots, int64_t gen_stride, int64_t capacity,
+                                  int ranks, uint32_t* state, uint8_t* out, int64_t nbytes,
+                                  uint32_t spin_limit, hipStream_t s) {
+  const int64_t items = nbytes / MXG_PACK_BYTES * ranks;
+  hipLaunchKernelGGL(collect_kernel, dim3(blocks_for(items)), dim3(kThreads), 0, s, slots,
+                     gen_stride, capacity, ranks, state, out, nbytes, spin_limit);
+  return hipGetLastError();
+}
+
+}  // namespace mxg

@@ -1,0 +1,67 @@
+// Internal declarations shared by the host API and the kernel files of the
+// MXFP8 publishing GEMM library (gfx950). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mxg {
+
+// Everything one GEMM+publish launch needs, by value.
+struct GemmArgs {
+  const uint8_t* w;   // [n, k] e4m3fn
+  const uint8_t* ws;  // [n, k/32] E8M0
+  const uint8_t* x;   // [m, k] e4m3fn
+  const uint8_t* xs;  // [m, k/32] E8M0
+  uint8_t* slot;      // mailbox slots + rank * capacity (generation 0)
+  int64_t gen_stride; // bytes between generations: ranks * capacity
+  uint32_t* state;    // mailbox state words
+  uint32_t* ws_hdr;   // split-K workspace header (null when split_k == 1)
+  uint64_t* pairs;    // split-K (value, epoch) pairs (null when split_k == 1)
+  uint16_t* c_out;    // raw BF16 output or null
+  int32_t m, n, k, split_k;
+  uint32_t spin_limit;
+};
+
+// A workgroup computes an output tile of n_tile = 16 * rb * wn rows for one
+// K slice; its 64 * wn * wk threads form wn x wk waves (wn along rows, wk
+// along K); each wave keeps `depth` K-blocks of W loads in flight.
+struct TileCfg {
+  int rb, wn, wk, depth;
+};
+
+inline int tile_rows(const TileCfg& c) { return 16 * c.rb * c.wn; }
+inline int tile_threads(const TileCfg& c) { return 64 * c.wn * c.wk; }
+
+// Dynamic LDS bytes of a launch (x slice, its scales, the partial tile).
+size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice);
+
+// The tile for a problem; MXG_TILE="rb,wn,wk,depth" forces one variant (and
+// fails when it does not fit). Returns false when no variant fits.
+bool choose_tile(int m, int n, int k, int split_k, TileCfg* out);
+
+// Whether a variant is compiled in.
+bool tile_available(const TileCfg& c);
+
+// How many workgroups of this variant can be resident at once on the current
+// device (CUs x blocks per CU); negative on a HIP error.
+long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes);
+
+// ev_start/ev_stop (may be null) are recorded around the kernel itself.
+hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t s,
+                               hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+
+// Mailbox kernels.
+hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);
+hipError_t launch_state_init(uint32_t* state, hipStream_t s);
+hipError_t launch_workspace_init(uint32_t* ws, size_t bytes, hipStream_t s);
+hipError_t launch_mailbox_publish(uint8_t* slot, int64_t gen_stride, uint32_t* state,
+                                  const uint8_t* src, int64_t nbytes, hipStream_t s);
+hipError_t launch_mailbox_collect(uint8_t* slots, int64_t gen_stride, int64_t capacity,
+                                  int ranks, uint32_t* state, uint8_t* out,
+                                  int64_t nbytes, uint32_t spin_limit, hipStream_t s);
+
+uint32_t spin_limit();
+
+}  // namespace mxg

@@ -1,0 +1,112 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def mx():
+    from mxfp8_decode_gemm_amd import build as b
+
+    if not os.path.exists(b.LIB):
+        b.build()
+    from mxfp8_decode_gemm_amd import binding
+
+    return binding
+
+
+def test_exports_every_declared_function(mx):
+    names = mx.header_functions()
+    assert len(names) == 14
+    lib = mx.library()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing
+
+
+def test_header_constants_match_binding(mx):
+    with open(os.path.join(ROOT, "include", "mxgemm.h")) as f:
+        h = f.read()
+    for name, val in [("MXG_GENERATIONS", 3), ("MXG_PACK_BYTES", 16), ("MXG_MAX_ROWS", 8),
+                      ("MXG_STATE_NEXT", 0), ("MXG_STATE_ACTIVE", 1), ("MXG_WS_EPOCH", 0)]:
+        assert f"#define {name} {val}" in h
+    assert "#define MXG_SENTINEL 0x80000000u" in h
+    assert mx.SENTINEL == 0x80000000 and mx.GENERATIONS == 3
+
+
+def test_sizes(mx):
+    assert mx.mxg_mailbox_slots_bytes(4, 65536) == 3 * 4 * 65536
+    assert mx.mxg_mailbox_slots_bytes(0, 64) == 0
+    assert mx.mxg_mailbox_slots_bytes(9, 64) == 0
+    assert mx.mxg_mailbox_slots_bytes(1, 24) == 0
+    assert mx.mxgemm_workspace_bytes(8, 7168, 8192, 1) == 0
+    assert mx.mxgemm_workspace_bytes(8, 7168, 8192, 4) == 256 + 4 * 64 * 7168
+
+
+def _mb(mx, slots=256, state=512, ranks=1, rank=0, cap=512):
+    mb = mx.mxg_mailbox()
+    mb.slots, mb.state, mb.ranks, mb.rank, mb.capacity_bytes = slots, state, ranks, rank, cap
+    return mb
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=0), -1), (dict(m=9), -1), (dict(n=12), -1), (dict(k=96), -1),
+    (dict(split_k=3), -1), (dict(split_k=8, k=512), -1), (dict(w=0), -1),
+    (dict(w=272 + 4), -2), (dict(x_scale=4096 + 8), -2), (dict(c_out=8200), -2),
+    (dict(n=512), -3), (dict(split_k=2), -4), (dict(split_k=2, ws=4096, ws_bytes=100), -4),
+])
+def test_publish_validation(mx, kw, code):
+    args = dict(w=4096, w_scale=4096, x=4096, x_scale=4096, m=1, n=256, k=512, split_k=1,
+                ws=None, ws_bytes=0, c_out=None)
+    args.update(kw)
+    mb = _mb(mx)
+    rc = mx.library().mxgemm_publish(ctypes.byref(mb), args["w"], args["w_scale"], args["x"],
+                                     args["x_scale"], args["m"], args["n"], args["k"],
+                                     args["split_k"], args["ws"], args["ws_bytes"],
+                                     args["c_out"], None)
+    assert rc == code
+
+
+def test_publish_validation_raises(mx):
+    mb = _mb(mx)
+    with pytest.raises(mx.MxgValueError):
+        mx.mxgemm_publish(mb, 4096, 4096, 4096, 4096, 9, 256, 512, 1, None, 0, None, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ranks=0), -1), (dict(ranks=9), -1), (dict(rank=1), -1), (dict(cap=24), -1),
+    (dict(slots=0), -1), (dict(slots=4100), -2),
+])
+def test_mailbox_init_validation(mx, kw, code):
+    a = dict(slots=4096, state=8192, ranks=1, rank=0, cap=512)
+    a.update(kw)
+    mb = mx.mxg_mailbox()
+    rc = mx.library().mailbox_init(ctypes.byref(mb), a["slots"], a["state"], a["ranks"],
+                                   a["rank"], a["cap"], None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("nbytes,code", [(0, -3), (24, -3), (1024, -3), (-16, -3)])
+def test_collect_and_publish_capacity(mx, nbytes, code):
+    mb = _mb(mx)
+    lib = mx.library()
+    assert lib.mailbox_collect(ctypes.byref(mb), 4096, nbytes, None) == code
+    assert lib.mailbox_publish(ctypes.byref(mb), 0, 4096, nbytes, None) == code
+    assert lib.mailbox_publish(ctypes.byref(mb), 1, 4096, 16, None) == -1
+    assert lib.mailbox_collect(ctypes.byref(mb), 4100, 16, None) == -2
+
+
+def test_misc(mx):
+    lib = mx.library()
+    assert mx.strerror(0) == "ok" and "aligned" in mx.strerror(-2)
+    prev = mx.mxg_set_spin_limit(123)
+    assert mx.mxg_set_spin_limit(prev) == 123
+    assert lib.mxg_graph_begin(None) == -1
+    assert lib.mxg_graph_launch(None, None) == -1
+    assert lib.mxg_graph_destroy(None) == -1
+    assert lib.mxgemm_workspace_init(None, 1024, None) == -1
+    assert lib.mxgemm_workspace_init(4100, 1024, None) == -2

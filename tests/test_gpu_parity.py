@@ -1,0 +1,354 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every case runs mxgemm_publish (+ mailbox_publish for emulated peers) and
+mailbox_collect through the C ABI and checks:
+  * raw BF16 outputs within the oracle tolerance (tests/../oracle/tolerance);
+  * the collected own slot bit-equal to the raw output with negative zero
+    cleared, and bit-equal to the oracle's bits wherever the values agree;
+  * peer slots bit-equal to the oracle mailbox model's output;
+  * no sentinel word and no negative-zero half in the output, the whole
+    mailbox back to the sentinel, and the state words as the model says.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    from mxfp8_decode_gemm_amd import binding as mx
+    from mxfp8_decode_gemm_amd import device as dv
+
+    torch.cuda.set_device(0)
+    return mx, dv
+
+
+def _oracle():
+    from oracle import codecs, gemm, mailbox, tolerance
+
+    return codecs, gemm, mailbox, tolerance
+
+
+def run_case(env, p, split_k=1, ranks=1, capacity=None, peers=None, calls=1, with_c=True,
+             ws=None):
+    """Run `calls` publish+collect rounds of problem p; check everything."""
+    mx, dv = env
+    codecs, gemm, mailbox, tolerance = _oracle()
+    cap = capacity or p.out_bytes
+    _say(f"case {p.name} seed={p.seed} m={p.m} n={p.n} k={p.k} split_k={split_k} ranks={ranks}")
+    ops = dv.Operands(p)
+    mbx = dv.Mailbox(ranks, cap)
+    if ws is None and split_k > 1:
+        ws = dv.Workspace(p.n, split_k)
+    epoch0 = ws.header()[mx.WS_EPOCH] if ws is not None else 0
+    c_out = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda") if with_c else None
+    model = mailbox.MailboxModel(ranks, cap)
+    bits, exact, abs_sum = gemm.gemm_publish_bits(p.w, p.ws, p.x, p.xs)
+    peer_dev = [dv.upload(peers[r - 1]) for r in range(1, ranks)] if ranks > 1 else []
+    outs = []
+    for _ in range(calls):
+        dv.publish(mbx, ops, split_k, ws, c_out)
+        for r in range(1, ranks):
+            mx.mailbox_publish(mbx.mb, r, peer_dev[r - 1], p.out_bytes)
+        outs.append(dv.collect(mbx, p.out_bytes))
+    torch.cuda.synchronize()
+    got = [dv.as_u16(o).reshape(ranks * p.m, p.n) for o in outs]
+    own = got[0][: p.m]
+    # values
+    if with_c:
+        raw = dv.as_u16(c_out).reshape(p.m, p.n)
+        ex = tolerance.excess(raw, exact, abs_sum)
+        assert np.all(ex <= 1.0), f"max excess {ex.max()} at {np.unravel_index(ex.argmax(), ex.shape)}"
+        assert np.array_equal(own, codecs.clear_negative_zero(raw))
+    else:
+        ex = tolerance.excess(own, exact, abs_sum)
+        assert np.all(ex <= 1.0)
+    same = codecs.bf16_to_f64(own) == codecs.bf16_to_f64(bits)
+    assert np.array_equal(own[same], bits[same])
+    # model: own slot from the device's values, peers from their payloads
+    for _ in range(calls):
+        model.publish(0, own)
+        for r in range(1, ranks):
+            model.publish(r, peers[r - 1])
+        expect = model.collect(p.out_bytes).reshape(ranks * p.m, p.n)
+    for g in got:
+        assert np.array_equal(g, expect)
+        assert not mailbox.check_collected(g)
+    assert not mailbox.check_idle_slots(mbx.slot_words())
+    st = mbx.state_words()
+    assert st[mx.STATE_NEXT] == model.next == calls % 3
+    assert st[mx.STATE_ERROR] == 0
+    if ws is not None:
+        hdr = ws.header()
+        assert hdr[mx.WS_EPOCH] == epoch0 + calls and hdr[mx.WS_ERROR] == 0
+        assert hdr[mx.WS_ARRIVALS] == 0
+    return own, bits, ex
+
+
+def test_tiny_config(env):
+    from workloads import generate
+
+    run_case(env, generate.config_problem(0), calls=4)
+
+
+@pytest.mark.parametrize("split_k", [1, 2, 4, 8])
+def test_small_all_splits(env, split_k):
+    from workloads import generate
+
+    p = generate.random_problem(31 + split_k, 8, 320, 2048, split_k)
+    run_case(env, p, split_k=split_k, calls=2)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 7, 8])
+def test_rows_and_ragged_n(env, m):
+    from workloads import generate
+
+    for n, k, s in [(8, 128, 1), (24, 384, 1), (40, 512, 2), (1000, 1024, 4), (136, 1024, 8)]:
+        p = generate.random_problem(1000 * m + n, m, n, k, s)
+        run_case(env, p, split_k=s)
+
+
+def test_single_nonzero_sweep(env):
+    """One nonzero W element and one nonzero x element at swept positions: the
+    result is one exact product, so any slip of the MFMA lane, K-piece or
+    scale mapping shows up bit for bit."""
+    mx, dv = env
+    codecs, gemm, _, _ = _oracle()
+    from workloads.generate import Problem
+
+    n, k, m = 64, 512, 8
+    rng = np.random.default_rng(7)
+    positions = [(r, kk, t) for r in (0, 5, 17, 34, 63) for kk in (0, 15, 16, 31, 32, 63, 64, 100,
+                                                                   127, 128, 200, 511)
+                 for t in (0, 3, 7)]
+    mbx = dv.Mailbox(1, 2 * m * n)
+    c_out = torch.empty(m * n, dtype=torch.int16, device="cuda")
+    for (r, kk, t) in positions:
+        w = np.zeros((n, k), np.uint8)
+        x = np.zeros((m, k), np.uint8)
+        ws = np.full((n, k // 32), 127, np.uint8)
+        xs = np.full((m, k // 32), 127, np.uint8)
+        w[r, kk] = rng.choice([0x38, 0xB9, 0x44, 0x51])
+        x[t, kk] = rng.choice([0x38, 0x3C, 0xC2])
+        ws[r, kk // 32] = rng.integers(118, 136)
+        xs[t, kk // 32] = rng.integers(118, 136)
+        # background scales of other blocks must not leak in
+        ws[r, (kk // 32 + 1) % (k // 32)] = 140
+        xs[t, (kk // 32 + 2) % (k // 32)] = 100
+        p = Problem("single", m, n, k, 1, w, ws, x, xs, 0)
+        dv.publish(mbx, dv.Operands(p), 1, None, c_out)
+        out = dv.collect(mbx, p.out_bytes)
+        torch.cuda.synchronize()
+        got = dv.as_u16(out).reshape(m, n)
+        bits, _, _ = gemm.gemm_publish_bits(w, ws, x, xs)
+        assert np.array_equal(got, bits), f"position {(r, kk, t)}"
+
+
+def test_closed_forms(env):
+    """Identity-like W returns x; all-ones x returns W's row sums."""
+    mx, dv = env
+    codecs, gemm, _, tolerance = _oracle()
+    from workloads import generate
+    from workloads.generate import Problem
+
+    base = generate.random_problem(8, 4, 256, 256)
+    w = np.zeros((256, 256), np.uint8)
+    w[np.arange(256), np.arange(256)] = 0x38
+    ws = np.full((256, 8), 127, np.uint8)
+    p = Problem("identity", 4, 256, 256, 1, w, ws, base.x, base.xs, 0)
+    own, bits, _ = run_case(env, p)
+    xd = codecs.decode_e4m3(base.x) * np.repeat(codecs.decode_e8m0(base.xs), 32, axis=1)
+    assert np.array_equal(codecs.bf16_to_f64(own), codecs.bf16_to_f64(codecs.bf16_rne_bits(xd)))
+    x1 = np.full((1, 256), 0x38, np.uint8)
+    xs1 = np.full((1, 8), 127, np.uint8)
+    p2 = Problem("ones", 1, 256, 256, 1, base.w, base.ws, x1, xs1, 0)
+    run_case(env, p2)
+
+
+def test_negative_zero_and_zero_rows(env):
+    from workloads import generate
+
+    p = generate.random_problem(77, 8, 512, 1024, 4, "stress")
+    own, bits, _ = run_case(env, p, split_k=4)
+    zr = np.r_[p.meta["zero_rows_pos"], p.meta["zero_rows_neg"], p.meta["tiny_rows"]]
+    assert np.all(own[:, zr] == 0)
+
+
+def test_fused_equals_unfused(env):
+    """The fused epilogue publishes the same bits as the raw output pushed
+    through the unfused publish (the consumer cannot tell them apart)."""
+    mx, dv = env
+    from workloads import generate
+
+    p = generate.random_problem(91, 8, 1024, 2048, 4, "stress")
+    ops = dv.Operands(p)
+    ws = dv.Workspace(p.n, 4)
+    a = dv.Mailbox(1, p.out_bytes)
+    b = dv.Mailbox(1, p.out_bytes)
+    c_out = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
+    dv.publish(a, ops, 4, ws, c_out)
+    mx.mailbox_publish(b.mb, 0, c_out, p.out_bytes)
+    sa = a.slot_words()
+    sb = b.slot_words()
+    assert np.array_equal(sa, sb)
+    oa = dv.collect(a, p.out_bytes)
+    ob = dv.collect(b, p.out_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
+
+
+def test_config1_full(env):
+    from workloads import generate
+
+    run_case(env, generate.config_problem(1))
+
+
+@pytest.mark.parametrize("dist", ["outliers", "normal"])
+def test_config2_full(env, dist):
+    from workloads import generate
+
+    p = generate.config_problem(2, dist=dist)
+    run_case(env, p, split_k=4, capacity=114688, calls=3)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+@pytest.mark.parametrize("split_k", [1, 4, 8])
+def test_config3_sweep(env, m, split_k):
+    from workloads import generate
+
+    p = generate.config_problem(3, m=m, split_k=split_k)
+    peers = generate.peer_payloads(p.seed, 4, m, p.n)
+    run_case(env, p, split_k=split_k, ranks=4, capacity=65536, peers=peers, calls=4)
+
+
+def test_config4_alternating(env):
+    """Alternating sizes through one mailbox and one workspace: every output
+    bit-identical to the first verified output of its size, nothing stale."""
+    mx, dv = env
+    codecs, gemm, mailbox, tolerance = _oracle()
+    from workloads import generate
+
+    probs = [generate.config_problem(4, size=s) for s in (0, 1)]
+    ops = [dv.Operands(p) for p in probs]
+    peers = [generate.peer_payloads(p.seed, 4, p.m, p.n) for p in probs]
+    peer_dev = [[dv.upload(pp[r]) for r in range(3)] for pp in peers]
+    mbx = dv.Mailbox(4, 32768)
+    ws = dv.Workspace(7168, 4)
+    c_out = [torch.empty(p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
+    model = mailbox.MailboxModel(4, 32768)
+    expect = [None, None]
+    calls = 60
+    for i in range(calls):
+        s = i % 2
+        p = probs[s]
+        dv.publish(mbx, ops[s], 4, ws, c_out[s])
+        for r in range(1, 4):
+            mx.mailbox_publish(mbx.mb, r, peer_dev[s][r - 1], p.out_bytes)
+        out = dv.as_u16(dv.collect(mbx, p.out_bytes)).reshape(4 * p.m, p.n)
+        if expect[s] is None:
+            raw = dv.as_u16(c_out[s]).reshape(p.m, p.n)
+            _, exact, abs_sum = gemm.gemm_publish_bits(p.w, p.ws, p.x, p.xs)
+            assert tolerance.within(raw, exact, abs_sum)
+            model.publish(0, raw)
+            for r in range(1, 4):
+                model.publish(r, peers[s][r - 1])
+            expect[s] = model.collect(p.out_bytes).reshape(4 * p.m, p.n)
+        assert np.array_equal(out, expect[s]), f"call {i}"
+        assert not mailbox.check_collected(out)
+        assert not mailbox.check_idle_slots(mbx.slot_words())
+    st = mbx.state_words()
+    assert st[mx.STATE_NEXT] == calls % 3 and st[mx.STATE_ERROR] == 0
+    assert ws.header()[mx.WS_EPOCH] == 1 + calls
+
+
+def test_graph_replays_match_eager(env):
+    mx, dv = env
+    from workloads import generate
+
+    p = generate.random_problem(55, 8, 2048, 4096, 4)
+    ops = dv.Operands(p)
+    mbx = dv.Mailbox(1, p.out_bytes)
+    ws = dv.Workspace(p.n, 4)
+    c_out = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
+    out = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        dv.publish(mbx, ops, 4, ws, c_out)
+        dv.collect(mbx, p.out_bytes, out)
+        stream.synchronize()
+        eager = out.clone()
+        mx.mxg_graph_begin(stream)
+        for _ in range(3):
+            dv.publish(mbx, ops, 4, ws, c_out)
+            dv.collect(mbx, p.out_bytes, out)
+        g = mx.mxg_graph_end(stream)
+        for rep in range(4):
+            out.zero_()
+            mx.mxg_graph_launch(g, stream)
+            stream.synchronize()
+            assert torch.equal(out, eager), f"replay {rep}"
+            # eager work between replays
+            dv.publish(mbx, ops, 4, ws, c_out)
+            dv.collect(mbx, p.out_bytes, out)
+            stream.synchronize()
+            assert torch.equal(out, eager)
+        mx.mxg_graph_destroy(g)
+    calls = 1 + 4 * 3 + 4
+    st = mbx.state_words()
+    assert st[mx.STATE_NEXT] == calls % 3
+    assert ws.header()[mx.WS_EPOCH] == 1 + calls
+
+
+def test_collect_spin_limit_sets_error(env):
+    """A rank that never publishes: with a tiny poll limit the collect gives
+    up, flags the error and still resets the slots (forced from the host; the
+    kernel exits normally)."""
+    mx, dv = env
+    from oracle import mailbox
+
+    mbx = dv.Mailbox(2, 256)
+    src = torch.ones(64, dtype=torch.int16, device="cuda")
+    mx.mailbox_publish(mbx.mb, 0, src, 128)
+    prev = mx.mxg_set_spin_limit(8)
+    try:
+        dv.collect(mbx, 128)
+        torch.cuda.synchronize()
+    finally:
+        mx.mxg_set_spin_limit(prev)
+    st = mbx.state_words()
+    assert st[mx.STATE_ERROR] & mx.ERR_COLLECT_SPIN
+    assert not mailbox.check_idle_slots(mbx.slot_words())
+    mbx.reinit()
+    torch.cuda.synchronize()
+    assert mbx.state_words()[mx.STATE_ERROR] == 0
+
+
+def test_stale_epoch_is_not_taken(env):
+    """Pairs left by an earlier call never carry the live tag: after a call of
+    one size, a call of another size that reuses the same pair addresses still
+    matches the oracle."""
+    from workloads import generate
+
+    mx, dv = env
+    a = generate.random_problem(61, 8, 1024, 4096, 8)
+    b = generate.random_problem(62, 2, 1024, 1024, 8)
+    c = generate.random_problem(63, 8, 512, 2048, 4)
+    ws = dv.Workspace(1024, 8)
+    run_case(env, a, split_k=8, ws=ws, calls=2)
+    run_case(env, b, split_k=8, ws=ws, calls=2)
+    run_case(env, c, split_k=4, ws=ws, calls=2)
+    run_case(env, a, split_k=8, ws=ws)
+    assert ws.header()[mx.WS_EPOCH] == 1 + 7
