@@ -107,6 +107,27 @@ size_t mxgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t split_k);
  * MXG_EALIGN, MXG_EHIP. */
 int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
+/* Packed weight layout. The GEMM streams W as 2048-byte tiles, one per
+ * (16-row block rb, 128-wide K block kb), in the order its lanes load them,
+ * so that every wave instruction reads 1 KB of contiguous HBM:
+ *   w_packed  + (rb*(k/128) + kb)*2048 + h*1024 + 16*l  (h = 0, 1; l = 0..63)
+ *             = the 16 bytes W[rb*16 + l%16][kb*128 + 64*h + 16*(l/16) .. +16)
+ *   ws_packed + ((rb*(k/128) + kb)*16 + r)*4
+ *             = the 4 scale bytes w_scale[rb*16 + r][kb*4 .. +4)
+ * Rows past n are zero codes with scale byte 127. The transform is a one-time
+ * re-layout at weight-load time (as FlashInfer's GEMM takes its own swizzled
+ * scale layout on the publishing_gemm page); it moves bytes only.
+ * Sizes: ceil(n/16)*16*k and ceil(n/16)*16*(k/32) bytes; 0 on bad sizes. */
+size_t mxgemm_packed_weight_bytes(int32_t n, int32_t k);
+size_t mxgemm_packed_scale_bytes(int32_t n, int32_t k);
+
+/* Re-lay row-major W [n, k] (e4m3fn) and w_scale [n, k/32] (E8M0) into the
+ * packed layout above. All four pointers are device memory, 16-B aligned;
+ * the outputs hold the sizes above. n % 8 == 0, k % 128 == 0. Enqueued on
+ * `stream`. Errors: MXG_EINVAL, MXG_EALIGN, MXG_EHIP. */
+int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int32_t k,
+                       uint8_t* w_packed, uint8_t* ws_packed, void* stream);
+
 /* The publishing GEMM (publishing_gemm page, module docstring, "GEMM
  * structure"; PublishingLowLatencyBlockscaledGemmKernel.epilog_warp and
  * publish_value):
@@ -120,8 +141,9 @@ int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
  * token (even column in the low half of each word). One thread then sets
  * state[ACTIVE] = that generation.
  *
- *   w        device, [n, k] e4m3fn bytes, row-major (k contiguous), 16-B aligned
- *   w_scale  device, [n, k/32] E8M0 bytes, row-major, 16-B aligned
+ *   w        device, W [n, k] e4m3fn in the packed layout (mxgemm_pack_weight),
+ *            16-B aligned
+ *   w_scale  device, its E8M0 scales in the packed layout, 16-B aligned
  *   x        device, [m, k] e4m3fn bytes, row-major, 16-B aligned
  *   x_scale  device, [m, k/32] E8M0 bytes, row-major, 16-B aligned
  *   m        activation rows, 1..8

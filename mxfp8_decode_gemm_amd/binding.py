@@ -83,6 +83,9 @@ def _load() -> ctypes.CDLL:
         "mailbox_init": (ctypes.c_int, [mbp, vp, vp, i32, i32, i64, vp]),
         "mxgemm_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "mxgemm_workspace_init": (ctypes.c_int, [vp, sz, vp]),
+        "mxgemm_packed_weight_bytes": (sz, [i32, i32]),
+        "mxgemm_packed_scale_bytes": (sz, [i32, i32]),
+        "mxgemm_pack_weight": (ctypes.c_int, [vp, vp, i32, i32, vp, vp, vp]),
         "mxgemm_publish": (ctypes.c_int, [mbp, vp, vp, vp, vp, i32, i32, i32, i32, vp, sz,
                                           vp, vp]),
         "mxgemm_publish_timed": (ctypes.c_int, [mbp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
@@ -189,6 +192,19 @@ def mxgemm_workspace_bytes(m: int, n: int, k: int, split_k: int) -> int:
 def mxgemm_workspace_init(workspace, workspace_bytes: int, stream=None) -> None:
     _check(_lib.mxgemm_workspace_init(_ptr(workspace), workspace_bytes, _stream(stream)),
            "mxgemm_workspace_init")
+
+
+def mxgemm_packed_weight_bytes(n: int, k: int) -> int:
+    return int(_lib.mxgemm_packed_weight_bytes(n, k))
+
+
+def mxgemm_packed_scale_bytes(n: int, k: int) -> int:
+    return int(_lib.mxgemm_packed_scale_bytes(n, k))
+
+
+def mxgemm_pack_weight(w, w_scale, n: int, k: int, w_packed, ws_packed, stream=None) -> None:
+    _check(_lib.mxgemm_pack_weight(_ptr(w), _ptr(w_scale), n, k, _ptr(w_packed),
+                                   _ptr(ws_packed), _stream(stream)), "mxgemm_pack_weight")
 
 
 def mxgemm_publish(mb: mxg_mailbox, w, w_scale, x, x_scale, m: int, n: int, k: int,

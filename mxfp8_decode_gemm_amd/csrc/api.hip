@@ -67,6 +67,26 @@ size_t mxgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t split_k) 
   return MXG_WS_HEADER_BYTES + (size_t)split_k * 8 * n8 * 8;
 }
 
+size_t mxgemm_packed_weight_bytes(int32_t n, int32_t k) {
+  if (n <= 0 || k <= 0 || k % 128) return 0;
+  return (size_t)((n + 15) / 16) * 16 * (size_t)k;
+}
+
+size_t mxgemm_packed_scale_bytes(int32_t n, int32_t k) {
+  if (n <= 0 || k <= 0 || k % 128) return 0;
+  return (size_t)((n + 15) / 16) * 16 * (size_t)(k / 32);
+}
+
+int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int32_t k,
+                       uint8_t* w_packed, uint8_t* ws_packed, void* stream) {
+  if (!w || !w_scale || !w_packed || !ws_packed) return MXG_EINVAL;
+  if (n <= 0 || n % 8 || k <= 0 || k % 128) return MXG_EINVAL;
+  if (!aligned16(w) || !aligned16(w_scale) || !aligned16(w_packed) || !aligned16(ws_packed))
+    return MXG_EALIGN;
+  return hip_code(launch_pack_weight(w, w_scale, n, k, w_packed, ws_packed,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || workspace_bytes < MXG_WS_HEADER_BYTES || workspace_bytes % 16)
     return MXG_EINVAL;
@@ -112,6 +132,7 @@ int publish_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale
   a.pairs = split_k > 1 ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
                                                        MXG_WS_HEADER_BYTES)
                         : nullptr;
+  a.pairs_bytes = split_k > 1 ? (int64_t)(workspace_bytes - MXG_WS_HEADER_BYTES) : 0;
   a.c_out = c_out;
   a.m = m;
   a.n = n;

@@ -62,6 +62,7 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // 2^(s-127) as an FP32 multiplier: the biased exponent s in the exponent
@@ -82,7 +83,7 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1, float sc
   return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-constexpr int kHeaderBytes = 16;  // LDS: [0] generation, [1] epoch
+constexpr int kHeaderBytes = 16;
 
 __device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -138,8 +139,11 @@ __device__ __forceinline__ void wave_sum(const float* red, int m, int ntile, int
 template <int NT>
 struct XStage {
   static constexpr int kChunks = 4;  // chunks per thread per round
+  static constexpr int kWords = 2;   // scale words per thread per round
   uint4 v0, v1, v2, v3;
   int d0, d1, d2, d3;
+  uint32_t s0, s1;
+  int e0, e1;
 
   __device__ __forceinline__ static int dest(int c, int cpr, int m) {
     const int t = c / cpr;
@@ -152,18 +156,36 @@ struct XStage {
     const int q = c - t * cpr;
     return *reinterpret_cast<const uint4*>(x + (size_t)t * K + k0 + 16 * q);
   }
+  // Loads are issued for every thread (an index past the slice re-reads the
+  // last chunk), so each wave issues the same number of loads and the
+  // compiler can wait for exactly these, not for the W loads issued later.
   __device__ __forceinline__ void load(const uint8_t* x, int K, size_t k0, int m, int cpr,
                                        int xch, int c0, int tid) {
-    const uint4 z = {0u, 0u, 0u, 0u};
     const int c_0 = c0 + tid, c_1 = c0 + NT + tid, c_2 = c0 + 2 * NT + tid, c_3 = c0 + 3 * NT + tid;
-    v0 = c_0 < xch ? src(x, K, k0, c_0, cpr) : z;
-    v1 = c_1 < xch ? src(x, K, k0, c_1, cpr) : z;
-    v2 = c_2 < xch ? src(x, K, k0, c_2, cpr) : z;
-    v3 = c_3 < xch ? src(x, K, k0, c_3, cpr) : z;
+    v0 = src(x, K, k0, c_0 < xch ? c_0 : xch - 1, cpr);
+    v1 = src(x, K, k0, c_1 < xch ? c_1 : xch - 1, cpr);
+    v2 = src(x, K, k0, c_2 < xch ? c_2 : xch - 1, cpr);
+    v3 = src(x, K, k0, c_3 < xch ? c_3 : xch - 1, cpr);
     d0 = c_0 < xch ? dest(c_0, cpr, m) : -1;
     d1 = c_1 < xch ? dest(c_1, cpr, m) : -1;
     d2 = c_2 < xch ? dest(c_2, cpr, m) : -1;
     d3 = c_3 < xch ? dest(c_3, cpr, m) : -1;
+  }
+  // Scale words: x_scale row t, word q of the slice -> LDS word t * wpr + q.
+  __device__ __forceinline__ void load_scales(const uint8_t* xs, int K, size_t k0, int wpr,
+                                              int nw, int c0, int tid) {
+    const int c_0 = c0 + tid, c_1 = c0 + NT + tid;
+    const int u0 = c_0 < nw ? c_0 : nw - 1, u1 = c_1 < nw ? c_1 : nw - 1;
+    s0 = *reinterpret_cast<const uint32_t*>(xs + (size_t)(u0 / wpr) * (K >> 5) + (k0 >> 5) +
+                                            4 * (u0 % wpr));
+    s1 = *reinterpret_cast<const uint32_t*>(xs + (size_t)(u1 / wpr) * (K >> 5) + (k0 >> 5) +
+                                            4 * (u1 % wpr));
+    e0 = c_0 < nw ? c_0 : -1;
+    e1 = c_1 < nw ? c_1 : -1;
+  }
+  __device__ __forceinline__ void store_scales(uint32_t* xsw) const {
+    if (e0 >= 0) xsw[e0] = s0;
+    if (e1 >= 0) xsw[e1] = s1;
   }
   __device__ __forceinline__ void store(uint4* xl) const {
     if (d0 >= 0) xl[d0] = v0;
@@ -173,8 +195,63 @@ struct XStage {
   }
 };
 
+
+// The rounds of x staging past the first, for slices larger than one round.
+// Kept out of line: its loads would otherwise make the compiler wait for every
+// W load in flight before the main loop of the common one-round case.
+template <int NT>
+__device__ __attribute__((noinline)) void stage_rest(const uint8_t* x, const uint8_t* xs, int K,
+                                                     size_t k0, int m, int cpr, int xch, int wpr,
+                                                     int nsw, int tid, uint4* xl, uint32_t* xsw) {
+  XStage<NT> st;
+  for (int c0 = XStage<NT>::kChunks * NT; c0 < xch; c0 += XStage<NT>::kChunks * NT) {
+    st.load(x, K, k0, m, cpr, xch, c0, tid);
+    st.store(xl);
+  }
+  for (int c0 = XStage<NT>::kWords * NT; c0 < nsw; c0 += XStage<NT>::kWords * NT) {
+    st.load_scales(xs, K, k0, wpr, nsw, c0, tid);
+    st.store_scales(xsw);
+  }
+}
+
+// Packs row-major W [n, k] and its scales [n, k/32] into the tile layout the
+// GEMM streams: row block rb (16 rows, zero rows past n), K block kb (128):
+//   w_packed  + (rb*K/128 + kb)*2048 + h*1024 + 16*l : 16 bytes of row
+//             rb*16 + l%16, K = kb*128 + 64*h + 16*(l/16) .. +16
+//   ws_packed + ((rb*K/128 + kb)*16 + r)*4            : the 4 scale bytes of
+//             row rb*16 + r for that K block (byte 127 past n)
+// One thread per 16-byte chunk; every index is checked against the sizes.
+__global__ void pack_weight_kernel(const uint8_t* w, const uint8_t* ws, int n, int k,
+                                   uint8_t* wp, uint8_t* wsp) {
+  const int kbt = k >> 7;
+  const int rbn = (n + 15) >> 4;
+  const size_t chunks = (size_t)rbn * kbt * 128;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += stride) {
+    const size_t t = c >> 7;
+    const int within = (int)(c & 127);
+    const int h = within >> 6, l = within & 63;
+    const int rb = (int)(t / kbt), kb = (int)(t - (size_t)rb * kbt);
+    const int row = rb * 16 + (l & 15);
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (row < n)
+      v = *reinterpret_cast<const uint4*>(w + (size_t)row * k + kb * 128 + 64 * h + 16 * (l >> 4));
+    reinterpret_cast<uint4*>(wp)[c] = v;
+    if (within < 16) {
+      const int r = within;
+      const int srow = rb * 16 + r;
+      uint32_t s = 0x7F7F7F7Fu;
+      if (srow < n)
+        s = *reinterpret_cast<const uint32_t*>(ws + (size_t)srow * (k >> 5) + kb * 4);
+      reinterpret_cast<uint32_t*>(wsp)[t * 16 + r] = s;
+    }
+  }
+}
+
+// At least two waves per SIMD (<= 256 VGPRs): with split-K the grid must be
+// resident at once, and a second wave hides the other's conversion work.
 template <int RB, int WN, int WK, int D, int SK>
-__global__ void __launch_bounds__(64 * WN * WK)
+__global__ void __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_publish_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr int NT = 64 * WN * WK;
@@ -205,76 +282,74 @@ gemm_publish_kernel(GemmArgs a) {
   uint4* xl = reinterpret_cast<uint4*>(lds + kHeaderBytes);
   uint8_t* xsl = lds + kHeaderBytes + (size_t)m * KS;
 
-  // ---- call hand-off: generation and epoch, read before arriving --------
-  // (all_gather page, _AllGatherKernel.kernel: each CTA reads the state once
-  // before it counts itself; the last CTA advances it.)
-  uint32_t gen = 0, epoch = 0, arrived = 0;
+  // ---- call hand-off: generation and epoch ------------------------------
+  // Read once per workgroup, before it counts itself (all_gather page,
+  // _AllGatherKernel.kernel: the last CTA to arrive advances the state). The
+  // loads are issued here and waited for only where the values are needed.
+  uint32_t gen = 0, epoch = 0;
   if (tid == 0) {
     gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
-    if (S > 1) {
-      epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH);
-      arrived = __hip_atomic_fetch_add(a.ws_hdr + MXG_WS_ARRIVALS, 1u, __ATOMIC_ACQ_REL,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (S > 1) epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH);
   }
 
   // ---- x slice -> LDS, first round (loads issued before the W stream) ----
   const int cpr = KS >> 4;  // 16-byte chunks per x row in the slice
   const int xch = m * cpr;
+  const int wpr = KS >> 7;  // x-scale words per token row in the slice
+  const int nsw = m * wpr;
   XStage<NT> xst;
   xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
+  xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
 
-  // ---- W stream prologue -------------------------------------------------
-  const uint8_t* wrow[RB];
-  const uint32_t* wsrow[RB];
+  // ---- x and its scales into LDS before any W load is issued ------------
+  // At kernel start the memory system is idle, so x lands in one short round
+  // trip; issued behind the W stream of every workgroup it would queue for
+  // microseconds and hold every wave at the barrier.
+  uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
+  xst.store(xl);
+  xst.store_scales(xsw);
+  if (xch > XStage<NT>::kChunks * NT || nsw > XStage<NT>::kWords * NT)
+    stage_rest<NT>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
+  // ---- W stream prologue (packed tiles, see mxgemm_pack_weight) ---------
+  // Tile (rb, kb) is 2048 contiguous bytes: lane l's K pieces at 16 l and
+  // 1024 + 16 l; its scales are 16 rows x 4 bytes. A wave streams the
+  // contiguous tiles kb0 .. kb0 + nbw - 1 of each of its row blocks.
+  const int KBT = K >> 7;                     // K blocks per row block
+  const int rbn = (N + 15) >> 4;              // packed row blocks
+  const int kb0 = slice * NB + kb_lo;         // first absolute K block of this wave
+  const uint8_t* wtile[RB];
+  const uint32_t* stile[RB];
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
-    int row = row0 + (wn * RB + i) * 16 + r16;
-    row = row < N ? row : N - 1;  // rows past N load row N-1; never published
-    wrow[i] = a.w + (size_t)row * K + kslice0 + 16 * grp;
-    wsrow[i] = reinterpret_cast<const uint32_t*>(a.ws + (size_t)row * (K >> 5) + (kslice0 >> 5));
+    int rb = (row0 >> 4) + wn * RB + i;
+    rb = rb < rbn ? rb : rbn - 1;  // row blocks past N load the last one; never published
+    wtile[i] = a.w + ((size_t)rb * KBT + kb0) * 2048 + 16 * lane;
+    stile[i] = reinterpret_cast<const uint32_t*>(a.ws) + ((size_t)rb * KBT + kb0) * 16 + r16;
   }
-  uint4 wlo[D][RB], whi[D][RB];
+  v4u wlo[D][RB], whi[D][RB];
   uint32_t wsc[D][RB];
+  // Block j of this wave, or (j < 0) an in-bounds dummy: the first 128 bytes
+  // of x and the first scale word of xs, which every workgroup reads anyway.
+  // Every refill slot issues its loads either way, so the count of loads in
+  // flight is the same on every path.
+  auto load_w = [&](int d, int j) __attribute__((always_inline)) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (d < nbw) {
-      const int kb = kb_lo + d;
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        wlo[d][i] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)kb * 128);
-        whi[d][i] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)kb * 128 + 64);
-        wsc[d][i] = wsrow[i][kb];
-      }
+    for (int i = 0; i < RB; ++i) {
+      const uint8_t* t = j >= 0 ? wtile[i] + (size_t)j * 2048 : a.x + 16 * (lane & 7);
+      const uint32_t* sc = j >= 0 ? stile[i] + (size_t)j * 16 : reinterpret_cast<const uint32_t*>(a.xs);
+      wlo[d][i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(t));
+      whi[d][i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(t + (j >= 0 ? 1024 : 0)));
+      wsc[d][i] = *sc;
     }
-  }
+  };
+  constexpr int G = D > 16 ? D : 16;  // K blocks per straight-line group
+  const int ng0 = nbw < G ? nbw : G;
+#pragma unroll
+  for (int d = 0; d < D; ++d) load_w(d, d < ng0 ? d : -1);
 
-  // ---- finish staging x and its scales ----------------------------------
-  xst.store(xl);
-  for (int c0 = XStage<NT>::kChunks * NT; c0 < xch; c0 += XStage<NT>::kChunks * NT) {
-    xst.load(a.x, K, kslice0, m, cpr, xch, c0, tid);
-    xst.store(xl);
-  }
-  {
-    const int wpr = KS >> 7;  // scale dwords per x row in the slice
-    const int nw = m * wpr;
-    for (int c = tid; c < nw; c += NT) {
-      const int t = c / wpr;
-      const int q = c - t * wpr;
-      reinterpret_cast<uint32_t*>(xsl)[c] =
-          *reinterpret_cast<const uint32_t*>(a.xs + (size_t)t * (K >> 5) + (kslice0 >> 5) + 4 * q);
-    }
-  }
   if (tid == 0) {
     hdr[0] = gen;
     hdr[1] = epoch;
-    if (S > 1 && arrived == gridDim.x - 1u) {
-      // Last workgroup of this launch to arrive: every workgroup has read the
-      // epoch, so the next launch may use the next one (never 0).
-      const uint32_t next = epoch + 1u == 0u ? 1u : epoch + 1u;
-      st_agent_u32(a.ws_hdr + MXG_WS_ARRIVALS, 0u);
-      st_agent_u32(a.ws_hdr + MXG_WS_EPOCH, next);
-    }
   }
   __syncthreads();
 
@@ -285,53 +360,65 @@ gemm_publish_kernel(GemmArgs a) {
   const bool tok = r16 < m;
   const int kspw = KS >> 5;  // scale bytes per x row in the slice
   const int sb0 = grp >> 1;  // 32-block of this lane's first 16 K (its second is sb0 + 2)
-  for (int base = 0; base < nbw; base += D) {
+  auto consume = [&](int d, int j) __attribute__((always_inline)) {
+    const int kb = kb_lo + j;  // K block within the slice
+    // B operand: x of this lane's token as exact BF16, four K steps.
+    v8bf bx[4];
+    if (tok) {
+      const uint4 xlo = xl[((kb * 2 + 0) * 4 + grp) * m + r16];
+      const uint4 xhi = xl[((kb * 2 + 1) * 4 + grp) * m + r16];
+      const uint8_t* xsr = xsl + r16 * kspw + kb * 4;
+      const float fs0 = e8m0_to_f32(xsr[sb0]);
+      const float fs1 = e8m0_to_f32(xsr[sb0 + 2]);
+      bx[0] = fp8x8_to_bf16(xlo.x, xlo.y, fs0);
+      bx[1] = fp8x8_to_bf16(xlo.z, xlo.w, fs0);
+      bx[2] = fp8x8_to_bf16(xhi.x, xhi.y, fs1);
+      bx[3] = fp8x8_to_bf16(xhi.z, xhi.w, fs1);
+    } else {
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int j = base + d;
-      if (j < nbw) {
-        const int kb = kb_lo + j;
-        // B operand: x of this lane's token, as exact BF16, four K steps.
-        v8bf bx[4];
-        if (tok) {
-          const uint4 xlo = xl[((kb * 2 + 0) * 4 + grp) * m + r16];
-          const uint4 xhi = xl[((kb * 2 + 1) * 4 + grp) * m + r16];
-          const uint8_t* xsr = xsl + r16 * kspw + kb * 4;
-          const float fs0 = e8m0_to_f32(xsr[sb0]);
-          const float fs1 = e8m0_to_f32(xsr[sb0 + 2]);
-          bx[0] = fp8x8_to_bf16(xlo.x, xlo.y, fs0);
-          bx[1] = fp8x8_to_bf16(xlo.z, xlo.w, fs0);
-          bx[2] = fp8x8_to_bf16(xhi.x, xhi.y, fs1);
-          bx[3] = fp8x8_to_bf16(xhi.z, xhi.w, fs1);
-        } else {
+      for (int q = 0; q < 4; ++q) bx[q] = v8bf{};
+    }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) bx[q] = v8bf{};
-        }
+    for (int i = 0; i < RB; ++i) {
+      const float fa0 = e8m0_to_f32((wsc[d][i] >> (8 * sb0)) & 0xFFu);
+      const float fa1 = e8m0_to_f32((wsc[d][i] >> (8 * (sb0 + 2))) & 0xFFu);
+      const v8bf a0 = fp8x8_to_bf16(wlo[d][i].x, wlo[d][i].y, fa0);
+      const v8bf a1 = fp8x8_to_bf16(wlo[d][i].z, wlo[d][i].w, fa0);
+      const v8bf a2 = fp8x8_to_bf16(whi[d][i].x, whi[d][i].y, fa1);
+      const v8bf a3 = fp8x8_to_bf16(whi[d][i].z, whi[d][i].w, fa1);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bx[0], acc[i], 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bx[1], acc[i], 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bx[2], acc[i], 0, 0, 0);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, bx[3], acc[i], 0, 0, 0);
+    }
+  };
+  // Straight-line groups of G blocks with a D-deep ring of W registers: step
+  // j consumes ring slot j % D and refills it with block j + D of the group
+  // (or a dummy), so no register is carried across a loop edge and the wait
+  // before each step is for exactly the loads D steps back. The first
+  // group's ring was filled above; later groups (more than G blocks per
+  // wave) refill it at their start.
+  for (int g0 = 0; g0 < nbw; g0 += G) {
+    const int ng = nbw - g0 < G ? nbw - g0 : G;
+    if (g0 > 0) {
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          const float fa0 = e8m0_to_f32((wsc[d][i] >> (8 * sb0)) & 0xFFu);
-          const float fa1 = e8m0_to_f32((wsc[d][i] >> (8 * (sb0 + 2))) & 0xFFu);
-          const v8bf a0 = fp8x8_to_bf16(wlo[d][i].x, wlo[d][i].y, fa0);
-          const v8bf a1 = fp8x8_to_bf16(wlo[d][i].z, wlo[d][i].w, fa0);
-          const v8bf a2 = fp8x8_to_bf16(whi[d][i].x, whi[d][i].y, fa1);
-          const v8bf a3 = fp8x8_to_bf16(whi[d][i].z, whi[d][i].w, fa1);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bx[0], acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bx[1], acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, bx[2], acc[i], 0, 0, 0);
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, bx[3], acc[i], 0, 0, 0);
-        }
-        if (j + D < nbw) {
-          const int kn = kb + D;
+      for (int d = 0; d < D; ++d) load_w(d, d < ng ? g0 + d : -1);
+    }
 #pragma unroll
-          for (int i = 0; i < RB; ++i) {
-            wlo[d][i] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)kn * 128);
-            whi[d][i] = *reinterpret_cast<const uint4*>(wrow[i] + (size_t)kn * 128 + 64);
-            wsc[d][i] = wsrow[i][kn];
-          }
-        }
-      }
+    for (int j = 0; j < G; ++j) {
+      if (j < ng) consume(j % D, g0 + j);
+      if (j + D < G) load_w(j % D, j + D < ng ? g0 + j + D : -1);
     }
   }
+
+  // Count this workgroup. Its epoch load returned before the LDS header was
+  // written, so it was performed before this count is issued; the count's
+  // result is needed only at the end, so its round trip overlaps the
+  // exchange. (A release here would write back the whole L2 per workgroup.)
+  uint32_t arrived = 0;
+  if (S > 1 && tid == 0)
+    arrived = __hip_atomic_fetch_add(a.ws_hdr + MXG_WS_ARRIVALS, 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- partial tile -> LDS [wk][t][row], summed over waves in K order ---
   __syncthreads();  // every wave is done with x in LDS
@@ -383,12 +470,14 @@ gemm_publish_kernel(GemmArgs a) {
       uint64_t pv[SK > 1 ? SK - 1 : 1][8];
       uint32_t polls = 0;
       for (;;) {
+        // Device-scope loads: a peer's pair may sit in another XCD's L2, and
+        // an L2-coherent load is not guaranteed to observe it.
 #pragma unroll
         for (int o = 0; o < SK - 1; ++o) {
           const int src = o < slice ? o : o + 1;
-          const uint64_t* p = a.pairs + (((size_t)src * 8 + t) * ncols + (n0 >> 3)) * 8;
+          const uint64_t* first = a.pairs + (((size_t)src * 8 + t) * ncols + (n0 >> 3)) * 8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pv[o][e] = ld_agent_u64(p + e);
+          for (int e = 0; e < 8; ++e) pv[o][e] = ld_agent_u64(first + e);
         }
         bool pending = false;
 #pragma unroll
@@ -445,6 +534,15 @@ gemm_publish_kernel(GemmArgs a) {
   // Hand the generation to the consumer once per grid (publishing_gemm page,
   // epilog_warp: block 0, one thread, sets the active stage word).
   if (blockIdx.x == 0 && tid == 0) st_agent_u32(a.state + MXG_STATE_ACTIVE, gen);
+  if (S > 1 && tid == 0 && arrived == gridDim.x - 1u) {
+    // Last workgroup to arrive: every other count was performed before this
+    // one returned grid - 1, and each followed its workgroup's completed
+    // epoch load; this store is issued after that return. So the next
+    // launch, and no workgroup of this one, sees the next epoch (never 0).
+    const uint32_t next = epoch + 1u == 0u ? 1u : epoch + 1u;
+    st_agent_u32(a.ws_hdr + MXG_WS_ARRIVALS, 0u);
+    st_agent_u32(a.ws_hdr + MXG_WS_EPOCH, next);
+  }
 }
 
 // ---- variant table --------------------------------------------------------
@@ -463,9 +561,9 @@ struct Variant {
 
 const Variant kVariants[] = {
     MXG_VARIANT(1, 1, 4, 4),  MXG_VARIANT(1, 1, 8, 4),  MXG_VARIANT(1, 1, 16, 4),
-    MXG_VARIANT(1, 1, 8, 8),  MXG_VARIANT(2, 1, 4, 4),  MXG_VARIANT(2, 1, 8, 2),
-    MXG_VARIANT(1, 2, 4, 4),  MXG_VARIANT(4, 1, 4, 4),  MXG_VARIANT(7, 1, 8, 2),
-    MXG_VARIANT(1, 7, 2, 8),  MXG_VARIANT(2, 1, 4, 8),  MXG_VARIANT(1, 1, 4, 8),
+    MXG_VARIANT(1, 4, 1, 16), MXG_VARIANT(1, 4, 1, 8),  MXG_VARIANT(1, 7, 1, 8),
+    MXG_VARIANT(1, 2, 2, 8),  MXG_VARIANT(1, 4, 2, 8),  MXG_VARIANT(2, 1, 4, 4),
+    MXG_VARIANT(4, 1, 4, 4),  MXG_VARIANT(1, 8, 1, 8),  MXG_VARIANT(2, 2, 2, 4),
 };
 
 const Variant* find_variant(const TileCfg& c, int split_k) {
@@ -509,8 +607,8 @@ bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
   // tiles wide enough to reuse the staged x, and (with split-K) a grid that
   // is resident at once.
   const int nb = ks / 128;
-  static const TileCfg kSplit[] = {{4, 1, 4, 4}, {7, 1, 8, 2}, {2, 1, 4, 4}, {1, 1, 4, 4},
-                                   {2, 1, 8, 2}, {1, 1, 8, 4}};
+  static const TileCfg kSplit[] = {{1, 7, 1, 8}, {1, 4, 1, 8}, {1, 4, 1, 16}, {1, 4, 2, 8},
+                                   {2, 1, 4, 4}, {1, 1, 4, 4}, {4, 1, 4, 4}};
   static const TileCfg kLongK[] = {{1, 1, 16, 4}, {1, 1, 8, 8}, {1, 1, 8, 4}, {1, 1, 4, 4}};
   static const TileCfg kShortK[] = {{1, 1, 4, 4}, {1, 1, 8, 4}, {2, 1, 4, 4}};
   const TileCfg* list;
@@ -563,6 +661,15 @@ long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes) {
   return r;
 }
 
+hipError_t launch_pack_weight(const uint8_t* w, const uint8_t* ws, int n, int k, uint8_t* wp,
+                              uint8_t* wsp, hipStream_t s) {
+  const size_t chunks = (size_t)((n + 15) / 16) * (k / 128) * 128;
+  const size_t blocks = std::min<size_t>((chunks + 255) / 256, 65536);
+  hipLaunchKernelGGL(pack_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, ws, n, k,
+                     wp, wsp);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t s,
                                hipEvent_t ev_start, hipEvent_t ev_stop) {
   const Variant* v = find_variant(c, a.split_k);
@@ -570,15 +677,16 @@ hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t 
   const int tiles = (a.n + tile_rows(c) - 1) / tile_rows(c);
   const dim3 grid(tiles * a.split_k), block(tile_threads(c));
   const size_t lds = gemm_lds_bytes(c, a.m, a.k / a.split_k);
+  GemmArgs args = a;
   if (lds > 64 * 1024) {
     const hipError_t e =
         hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  void* args[] = {const_cast<GemmArgs*>(&a)};
+  void* kargs[] = {&args};
   if (ev_start || ev_stop)
-    return hipExtLaunchKernel(v->fn, grid, block, args, lds, s, ev_start, ev_stop, 0);
-  return hipLaunchKernel(v->fn, grid, block, args, lds, s);
+    return hipExtLaunchKernel(v->fn, grid, block, kargs, lds, s, ev_start, ev_stop, 0);
+  return hipLaunchKernel(v->fn, grid, block, kargs, lds, s);
 }
 
 }  // namespace mxg

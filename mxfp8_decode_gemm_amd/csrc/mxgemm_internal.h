@@ -10,8 +10,8 @@ namespace mxg {
 
 // Everything one GEMM+publish launch needs, by value.
 struct GemmArgs {
-  const uint8_t* w;   // [n, k] e4m3fn
-  const uint8_t* ws;  // [n, k/32] E8M0
+  const uint8_t* w;   // packed W tiles (mxgemm_pack_weight)
+  const uint8_t* ws;  // packed scales
   const uint8_t* x;   // [m, k] e4m3fn
   const uint8_t* xs;  // [m, k/32] E8M0
   uint8_t* slot;      // mailbox slots + rank * capacity (generation 0)
@@ -19,6 +19,7 @@ struct GemmArgs {
   uint32_t* state;    // mailbox state words
   uint32_t* ws_hdr;   // split-K workspace header (null when split_k == 1)
   uint64_t* pairs;    // split-K (value, epoch) pairs (null when split_k == 1)
+  int64_t pairs_bytes; // bytes of the pairs region
   uint16_t* c_out;    // raw BF16 output or null
   int32_t m, n, k, split_k;
   uint32_t spin_limit;
@@ -51,6 +52,10 @@ long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes);
 // ev_start/ev_stop (may be null) are recorded around the kernel itself.
 hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t s,
                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+
+// Packs row-major W and scales into the GEMM's tile layout.
+hipError_t launch_pack_weight(const uint8_t* w, const uint8_t* ws, int n, int k, uint8_t* wp,
+                              uint8_t* wsp, hipStream_t s);
 
 // Mailbox kernels.
 hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);

@@ -67,13 +67,22 @@ class Workspace:
         return self.buf[: mx.WS_HEADER_BYTES // 4].cpu().numpy().view(np.uint32).copy()
 
 
+def pack_weight(w: torch.Tensor, ws: torch.Tensor, n: int, k: int, stream=None):
+    """Device copies of W and its scales in the GEMM's packed tile layout."""
+    wp = torch.empty(mx.mxgemm_packed_weight_bytes(n, k), dtype=torch.uint8, device=w.device)
+    wsp = torch.empty(mx.mxgemm_packed_scale_bytes(n, k), dtype=torch.uint8, device=w.device)
+    mx.mxgemm_pack_weight(w, ws, n, k, wp, wsp, stream)
+    return wp, wsp
+
+
 class Operands:
-    """A problem's MXFP8 operands in HBM."""
+    """A problem's MXFP8 operands in HBM; W and its scales packed once."""
 
     def __init__(self, problem, device=None) -> None:
         self.m, self.n, self.k = problem.m, problem.n, problem.k
-        self.w = upload(problem.w, device)
-        self.ws = upload(problem.ws, device)
+        w = upload(problem.w, device)
+        ws = upload(problem.ws, device)
+        self.w, self.ws = pack_weight(w, ws, self.n, self.k)
         self.x = upload(problem.x, device)
         self.xs = upload(problem.xs, device)
 

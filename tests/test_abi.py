@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -98,6 +98,18 @@ def test_collect_and_publish_capacity(mx, nbytes, code):
     assert lib.mailbox_publish(ctypes.byref(mb), 0, 4096, nbytes, None) == code
     assert lib.mailbox_publish(ctypes.byref(mb), 1, 4096, 16, None) == -1
     assert lib.mailbox_collect(ctypes.byref(mb), 4100, 16, None) == -2
+
+
+def test_pack_sizes_and_validation(mx):
+    assert mx.mxgemm_packed_weight_bytes(7168, 8192) == 7168 * 8192
+    assert mx.mxgemm_packed_weight_bytes(24, 128) == 32 * 128
+    assert mx.mxgemm_packed_scale_bytes(24, 128) == 32 * 4
+    assert mx.mxgemm_packed_weight_bytes(8, 96) == 0
+    lib = mx.library()
+    assert lib.mxgemm_pack_weight(4096, 4096, 12, 128, 4096, 4096, None) == -1
+    assert lib.mxgemm_pack_weight(4096, 4096, 16, 100, 4096, 4096, None) == -1
+    assert lib.mxgemm_pack_weight(None, 4096, 16, 128, 4096, 4096, None) == -1
+    assert lib.mxgemm_pack_weight(4100, 4096, 16, 128, 4096, 4096, None) == -2
 
 
 def test_misc(mx):

@@ -352,3 +352,37 @@ def test_stale_epoch_is_not_taken(env):
     run_case(env, c, split_k=4, ws=ws, calls=2)
     run_case(env, a, split_k=8, ws=ws)
     assert ws.header()[mx.WS_EPOCH] == 1 + 7
+
+
+@pytest.mark.parametrize("n,k", [(16, 128), (24, 384), (136, 1024), (1000, 512)])
+def test_pack_weight_layout(env, n, k):
+    """mxgemm_pack_weight moves bytes only: compare with the layout written
+    out element by element (byte work is bit-exact)."""
+    mx, dv = env
+    rng = np.random.default_rng(n + k)
+    w = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    ws = rng.integers(0, 256, size=(n, k // 32), dtype=np.uint8)
+    wp, wsp = dv.pack_weight(dv.upload(w), dv.upload(ws), n, k)
+    torch.cuda.synchronize()
+    wp = wp.cpu().numpy()
+    wsp = wsp.cpu().numpy()
+    rbn, kbt = -(-n // 16), k // 128
+    assert wp.size == rbn * kbt * 2048 and wsp.size == rbn * kbt * 64
+    expect = np.zeros(rbn * kbt * 2048, np.uint8)
+    sexp = np.full(rbn * kbt * 64, 127, np.uint8)
+    for rb in range(rbn):
+        for kb in range(kbt):
+            t = rb * kbt + kb
+            for h in range(2):
+                for l in range(64):
+                    row = rb * 16 + l % 16
+                    if row < n:
+                        col = kb * 128 + 64 * h + 16 * (l // 16)
+                        o = t * 2048 + h * 1024 + 16 * l
+                        expect[o:o + 16] = w[row, col:col + 16]
+            for r in range(16):
+                row = rb * 16 + r
+                if row < n:
+                    sexp[(t * 16 + r) * 4:(t * 16 + r) * 4 + 4] = ws[row, kb * 4:kb * 4 + 4]
+    assert np.array_equal(wp, expect)
+    assert np.array_equal(wsp, sexp)
