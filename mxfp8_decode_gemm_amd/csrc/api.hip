@@ -133,6 +133,7 @@ int publish_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale
                                                        MXG_WS_HEADER_BYTES)
                         : nullptr;
   a.pairs_bytes = split_k > 1 ? (int64_t)(workspace_bytes - MXG_WS_HEADER_BYTES) : 0;
+  a.xcd_groups = 0;
   a.c_out = c_out;
   a.m = m;
   a.n = n;

@@ -113,26 +113,6 @@ __device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
   return lo | hi;
 }
 
-// Sum of the wave partials of pack (t, jc) in ascending K order: the waves
-// of a workgroup cover its K slice in order wk = 0, 1, ...
-template <int WK>
-__device__ __forceinline__ void wave_sum(const float* red, int m, int ntile, int t, int jc,
-                                         float v[8]) {
-  const float* src = red + (size_t)t * ntile + 8 * jc;
-  const v4f p0 = *reinterpret_cast<const v4f*>(src);
-  const v4f p1 = *reinterpret_cast<const v4f*>(src + 4);
-  v[0] = p0[0]; v[1] = p0[1]; v[2] = p0[2]; v[3] = p0[3];
-  v[4] = p1[0]; v[5] = p1[1]; v[6] = p1[2]; v[7] = p1[3];
-#pragma unroll
-  for (int w = 1; w < WK; ++w) {
-    const float* s2 = red + (size_t)(w * m + t) * ntile + 8 * jc;
-    const v4f q0 = *reinterpret_cast<const v4f*>(s2);
-    const v4f q1 = *reinterpret_cast<const v4f*>(s2 + 4);
-    v[0] += q0[0]; v[1] += q0[1]; v[2] += q0[2]; v[3] += q0[3];
-    v[4] += q1[0]; v[5] += q1[1]; v[6] += q1[2]; v[7] += q1[3];
-  }
-}
-
 // Copies x chunks (16 bytes) of the workgroup's K slice into LDS in the order
 // the MFMA B operand reads them: chunk (kb, half, group, t) holds
 // x[t][kb*128 + 64*half + 16*group .. +16).
@@ -267,8 +247,19 @@ gemm_publish_kernel(GemmArgs a) {
   const int grp = lane >> 4;  // lane group: K pieces and scale block
 
   constexpr int S = SK;  // split-K slices (the launch's split_k)
-  const int tile = blockIdx.x / S;
-  const int slice = blockIdx.x - tile * S;
+  // Workgroups are handed to the 8 XCDs round-robin by index. When the
+  // tiles divide evenly, the S slices of a tile get indices 8 apart, so they
+  // run on one XCD and their pair exchange stays within its L2. Placement
+  // only affects speed: the exchange is correct for any placement.
+  int tile, slice;
+  if (S > 1 && a.xcd_groups) {
+    const int b = blockIdx.x, q = b >> 3;
+    slice = q % S;
+    tile = (q / S) * 8 + (b & 7);
+  } else {
+    tile = blockIdx.x / S;
+    slice = blockIdx.x - tile * S;
+  }
   const int m = a.m, N = a.n, K = a.k;
   const int KS = K / S;             // K slice of this workgroup
   const int NB = KS >> 7;           // 128-wide K blocks in the slice
@@ -292,7 +283,7 @@ gemm_publish_kernel(GemmArgs a) {
     if (S > 1) epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH);
   }
 
-  // ---- x slice -> LDS, first round (loads issued before the W stream) ----
+  // ---- x slice, first round: loads issued before the W stream -----------
   const int cpr = KS >> 4;  // 16-byte chunks per x row in the slice
   const int xch = m * cpr;
   const int wpr = KS >> 7;  // x-scale words per token row in the slice
@@ -301,15 +292,6 @@ gemm_publish_kernel(GemmArgs a) {
   xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
   xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
 
-  // ---- x and its scales into LDS before any W load is issued ------------
-  // At kernel start the memory system is idle, so x lands in one short round
-  // trip; issued behind the W stream of every workgroup it would queue for
-  // microseconds and hold every wave at the barrier.
-  uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
-  xst.store(xl);
-  xst.store_scales(xsw);
-  if (xch > XStage<NT>::kChunks * NT || nsw > XStage<NT>::kWords * NT)
-    stage_rest<NT>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
   // ---- W stream prologue (packed tiles, see mxgemm_pack_weight) ---------
   // Tile (rb, kb) is 2048 contiguous bytes: lane l's K pieces at 16 l and
   // 1024 + 16 l; its scales are 16 rows x 4 bytes. A wave streams the
@@ -347,6 +329,14 @@ gemm_publish_kernel(GemmArgs a) {
 #pragma unroll
   for (int d = 0; d < D; ++d) load_w(d, d < ng0 ? d : -1);
 
+  // ---- x and its scales into LDS ---------------------------------------
+  // The x loads were issued first, so waiting for them leaves the W prologue
+  // in flight: the W stream starts at once and x lands in one round trip.
+  uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
+  xst.store(xl);
+  xst.store_scales(xsw);
+  if (xch > XStage<NT>::kChunks * NT || nsw > XStage<NT>::kWords * NT)
+    stage_rest<NT>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
   if (tid == 0) {
     hdr[0] = gen;
     hdr[1] = epoch;
@@ -411,12 +401,38 @@ gemm_publish_kernel(GemmArgs a) {
     }
   }
 
+  // ---- roles after the main loop ---------------------------------------
+  // Each 16-byte pack (8 columns of one token) is reduced by one slice: in
+  // every token row of the tile, slice s owns the pack columns
+  // jc in [ceil(s * PPR / S), ceil((s + 1) * PPR / S)), a contiguous run.
+  // With split-K the first PW waves handle the owned packs (poll, reduce,
+  // publish), one lane per column, and the other waves send the partials
+  // the other slices own. Loads and stores share one in-order completion
+  // counter per wave, so a polling wave must have no store of its own in
+  // flight: its poll then returns as soon as the peers' pairs are there.
+  // Without split-K every wave publishes.
+  constexpr int NW = NT / 64;
+  constexpr int PPR = NTILE / 8;  // packs per token row of the tile
+  const int jlo = (slice * PPR + SK - 1) / SK;
+  const int jhi = ((slice + 1) * PPR + SK - 1) / SK;
+  const int cnt = jhi - jlo;           // owned packs per token row
+  const int own_items = m * cnt * 8;   // one lane per owned (pack, column)
+  int pw = NW;
+  if (SK > 1 && NW > 1) {
+    pw = (own_items + 63) >> 6;
+    pw = pw < 1 ? 1 : (pw > NW - 1 ? NW - 1 : pw);
+  }
+  const bool poller = wave < pw;
+  const bool sender = SK > 1 && (NW == 1 || wave >= pw);
+  const int counter_tid = NW > 1 ? NT - 64 : 0;  // first lane of the last wave
+
   // Count this workgroup. Its epoch load returned before the LDS header was
   // written, so it was performed before this count is issued; the count's
-  // result is needed only at the end, so its round trip overlaps the
-  // exchange. (A release here would write back the whole L2 per workgroup.)
+  // result is needed only at the end, and it is issued by a wave that never
+  // polls, so its round trip delays no poll. (A release here would write
+  // back the whole L2 per workgroup.)
   uint32_t arrived = 0;
-  if (S > 1 && tid == 0)
+  if (S > 1 && tid == counter_tid)
     arrived = __hip_atomic_fetch_add(a.ws_hdr + MXG_WS_ARRIVALS, 1u, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
 
@@ -433,108 +449,107 @@ gemm_publish_kernel(GemmArgs a) {
   __syncthreads();
   gen = hdr[0];
   epoch = hdr[1];
-
-  // ---- one thread per pack: split-K exchange, BF16, publish -------------
-  constexpr int PPR = NTILE / 8;  // packs per token row of the tile
-  const int npacks = m * PPR;
   uint8_t* slot = a.slot + (size_t)gen * a.gen_stride;
   const size_t ncols = (size_t)(N >> 3);
-  // Pass 1 (split-K only): store the partial packs other slices own. Every
-  // send is issued before this thread polls anything, so no two workgroups
-  // can wait on each other.
-  if (SK > 1) {
-    for (int P = tid; P < npacks; P += NT) {
-      const int t = P / PPR;
-      const int jc = P - t * PPR;
-      const int n0 = row0 + 8 * jc;
-      if (n0 >= N || P % SK == slice) continue;
-      float v[8];
-      wave_sum<WK>(red, m, NTILE, t, jc, v);
-      // pairs[(slice * 8 + t) * (N / 8) + n / 8][0..7]
-      uint64_t* dst = a.pairs + (((size_t)slice * 8 + t) * ncols + (n0 >> 3)) * 8;
+  // This workgroup's partial of tile row `row` (within the tile), token t.
+  auto partial = [&](int t, int row) __attribute__((always_inline)) {
+    float v = red[(size_t)t * NTILE + row];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        st_agent_u64(dst + e, (uint64_t)__float_as_uint(v[e]) | ((uint64_t)epoch << 32));
+    for (int w = 1; w < WK; ++w) v += red[(size_t)(w * m + t) * NTILE + row];
+    return v;
+  };
+
+  // ---- sends: one (FP32 bits, epoch) pair per lane ----------------------
+  // pairs[((slice * 8 + t) * (N / 8) + n / 8) * 8 + n % 8]; lanes take
+  // consecutive columns of a token row, so a wave writes whole packs.
+  if (sender) {
+    const int s0 = NW == 1 ? tid : tid - pw * 64;
+    const int ns = NW == 1 ? NT : NT - pw * 64;
+    for (int q = s0; q < m * NTILE; q += ns) {
+      const int t = q / NTILE;
+      const int row = q - t * NTILE;
+      const int jc = row >> 3;
+      if (row0 + row >= N || (jc >= jlo && jc < jhi)) continue;
+      st_agent_u64(a.pairs + ((size_t)slice * 8 + t) * ncols * 8 + row0 + row,
+                   (uint64_t)__float_as_uint(partial(t, row)) | ((uint64_t)epoch << 32));
     }
   }
-  // Pass 2: the packs this slice owns (all of them without split-K).
-  for (int P = tid; P < npacks; P += NT) {
-    const int t = P / PPR;
-    const int jc = P - t * PPR;
-    const int n0 = row0 + 8 * jc;
-    if (n0 >= N || (SK > 1 && P % SK != slice)) continue;
-    float v[8];
-    wave_sum<WK>(red, m, NTILE, t, jc, v);
-    if (SK > 1) {
-      // Poll the other slices' pairs of this pack in one batch.
-      uint64_t pv[SK > 1 ? SK - 1 : 1][8];
-      uint32_t polls = 0;
-      for (;;) {
-        // Device-scope loads: a peer's pair may sit in another XCD's L2, and
-        // an L2-coherent load is not guaranteed to observe it.
+
+  // ---- owned packs: exchange, BF16, publish -----------------------------
+  // Lane 8j + e of a wave takes column e of one owned pack; the eight lanes
+  // of a pack stay together (every count below is a multiple of 8), so the
+  // pack's BF16 values meet in its lane e = 0 for one 16-byte store.
+  if (poller) {
+    const int e = lane & 7;
+    for (int i0 = wave * 64; i0 < own_items; i0 += pw * 64) {
+      const int item = i0 + lane;
+      const int pk = item >> 3;  // owned pack index: token row t, run position
+      const int t = cnt > 0 ? pk / cnt : 0;
+      const int jc = jlo + (pk - t * cnt);
+      const int row = 8 * jc + e;
+      const bool live = item < own_items && row0 + 8 * jc < N;
+      float v = live ? partial(t, row) : 0.f;
+      if (SK > 1) {
+        // Poll the other slices' pairs of this column in one batch.
+        uint64_t pv[SK > 1 ? SK - 1 : 1];
+        uint32_t polls = 0;
+        for (;;) {
+          bool pending = false;
+          if (live) {
+            // Device-scope loads: a peer's pair may sit in another XCD's
+            // L2, and an L2-coherent load is not guaranteed to observe it.
 #pragma unroll
-        for (int o = 0; o < SK - 1; ++o) {
-          const int src = o < slice ? o : o + 1;
-          const uint64_t* first = a.pairs + (((size_t)src * 8 + t) * ncols + (n0 >> 3)) * 8;
+            for (int o = 0; o < SK - 1; ++o) {
+              const int src = o < slice ? o : o + 1;
+              pv[o] = ld_agent_u64(a.pairs + ((size_t)src * 8 + t) * ncols * 8 + row0 + row);
+            }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pv[o][e] = ld_agent_u64(first + e);
-        }
-        bool pending = false;
-#pragma unroll
-        for (int o = 0; o < SK - 1; ++o)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pending |= (uint32_t)(pv[o][e] >> 32) != epoch;
-        if (!pending) break;
-        if (++polls >= a.spin_limit) {
-          __hip_atomic_fetch_or(a.ws_hdr + MXG_WS_ERROR, MXG_ERR_SPLITK_SPIN, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      // Sum the slices in ascending K order, this slice's partial in place:
-      // slot o of pv holds slice o for o < slice and slice o + 1 above it.
-      float r[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = slice == 0 ? v[e] : __uint_as_float((uint32_t)pv[0][e]);
-#pragma unroll
-      for (int o = 1; o < SK; ++o) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float term;
-          if (o == slice) {
-            term = v[e];
-          } else if (o < slice) {
-            term = __uint_as_float((uint32_t)pv[o][e]);
-          } else {
-            term = __uint_as_float((uint32_t)pv[o - 1][e]);
+            for (int o = 0; o < SK - 1; ++o) pending |= (uint32_t)(pv[o] >> 32) != epoch;
           }
-          r[e] += term;
+          if (!pending) break;
+          if (++polls >= a.spin_limit) {
+            __hip_atomic_fetch_or(a.ws_hdr + MXG_WS_ERROR, MXG_ERR_SPLITK_SPIN, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        // Sum the slices in ascending K order, this slice's partial in
+        // place: pv[o] holds slice o below this slice and o + 1 above it.
+        if (live) {
+          float r = slice == 0 ? v : __uint_as_float((uint32_t)pv[0]);
+#pragma unroll
+          for (int o = 1; o < SK; ++o)
+            r += o == slice ? v : __uint_as_float((uint32_t)pv[o < slice ? o : o - 1]);
+          v = r;
         }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = r[e];
+      // BF16 (nearest even) of this column, then the pack's eight halves
+      // gathered into lane e = 0: raw store, negative-zero clear, publish.
+      const __bf16 hb = (__bf16)v;
+      const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, hb);
+      const uint32_t pair = h | ((uint32_t)__shfl_down(h, 1, 64) << 16);
+      const uint32_t p1 = __shfl_down(pair, 2, 64);
+      const uint32_t p2 = __shfl_down(pair, 4, 64);
+      const uint32_t p3 = __shfl_down(pair, 6, 64);
+      if (live && e == 0) {
+        const uint4 raw = {pair, p1, p2, p3};
+        const size_t off = ((size_t)t * N + row0 + 8 * jc) * 2;
+        if (a.c_out) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.c_out) + off) = raw;
+        uint4 clean;
+        clean.x = clear_negative_zero(raw.x);
+        clean.y = clear_negative_zero(raw.y);
+        clean.z = clear_negative_zero(raw.z);
+        clean.w = clear_negative_zero(raw.w);
+        *reinterpret_cast<uint4*>(slot + off) = clean;
+      }
     }
-    // BF16 (nearest even), raw store, negative-zero clear, 16-byte publish.
-    uint4 raw;
-    raw.x = bf16_pair(v[0], v[1]);
-    raw.y = bf16_pair(v[2], v[3]);
-    raw.z = bf16_pair(v[4], v[5]);
-    raw.w = bf16_pair(v[6], v[7]);
-    const size_t off = ((size_t)t * N + n0) * 2;
-    if (a.c_out) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.c_out) + off) = raw;
-    uint4 clean;
-    clean.x = clear_negative_zero(raw.x);
-    clean.y = clear_negative_zero(raw.y);
-    clean.z = clear_negative_zero(raw.z);
-    clean.w = clear_negative_zero(raw.w);
-    *reinterpret_cast<uint4*>(slot + off) = clean;
   }
 
   // Hand the generation to the consumer once per grid (publishing_gemm page,
   // epilog_warp: block 0, one thread, sets the active stage word).
   if (blockIdx.x == 0 && tid == 0) st_agent_u32(a.state + MXG_STATE_ACTIVE, gen);
-  if (S > 1 && tid == 0 && arrived == gridDim.x - 1u) {
+  if (S > 1 && tid == counter_tid && arrived == gridDim.x - 1u) {
     // Last workgroup to arrive: every other count was performed before this
     // one returned grid - 1, and each followed its workgroup's completed
     // epoch load; this store is issued after that return. So the next
@@ -563,7 +578,7 @@ const Variant kVariants[] = {
     MXG_VARIANT(1, 1, 4, 4),  MXG_VARIANT(1, 1, 8, 4),  MXG_VARIANT(1, 1, 16, 4),
     MXG_VARIANT(1, 4, 1, 16), MXG_VARIANT(1, 4, 1, 8),  MXG_VARIANT(1, 7, 1, 8),
     MXG_VARIANT(1, 2, 2, 8),  MXG_VARIANT(1, 4, 2, 8),  MXG_VARIANT(2, 1, 4, 4),
-    MXG_VARIANT(4, 1, 4, 4),  MXG_VARIANT(1, 8, 1, 8),  MXG_VARIANT(2, 2, 2, 4),
+    MXG_VARIANT(1, 8, 1, 8),  MXG_VARIANT(2, 2, 2, 4),  MXG_VARIANT(1, 7, 1, 16),
 };
 
 const Variant* find_variant(const TileCfg& c, int split_k) {
@@ -608,7 +623,7 @@ bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
   // is resident at once.
   const int nb = ks / 128;
   static const TileCfg kSplit[] = {{1, 7, 1, 8}, {1, 4, 1, 8}, {1, 4, 1, 16}, {1, 4, 2, 8},
-                                   {2, 1, 4, 4}, {1, 1, 4, 4}, {4, 1, 4, 4}};
+                                   {2, 1, 4, 4}, {1, 1, 4, 4}};
   static const TileCfg kLongK[] = {{1, 1, 16, 4}, {1, 1, 8, 8}, {1, 1, 8, 4}, {1, 1, 4, 4}};
   static const TileCfg kShortK[] = {{1, 1, 4, 4}, {1, 1, 8, 4}, {2, 1, 4, 4}};
   const TileCfg* list;
@@ -678,6 +693,7 @@ hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t 
   const dim3 grid(tiles * a.split_k), block(tile_threads(c));
   const size_t lds = gemm_lds_bytes(c, a.m, a.k / a.split_k);
   GemmArgs args = a;
+  args.xcd_groups = a.split_k > 1 && tiles % 8 == 0 ? 1 : 0;
   if (lds > 64 * 1024) {
     const hipError_t e =
         hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

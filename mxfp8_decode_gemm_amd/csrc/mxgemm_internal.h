@@ -23,6 +23,7 @@ struct GemmArgs {
   uint16_t* c_out;    // raw BF16 output or null
   int32_t m, n, k, split_k;
   uint32_t spin_limit;
+  int32_t xcd_groups; // set by the launcher: the slices of a tile share an XCD
 };
 
 // A workgroup computes an output tile of n_tile = 16 * rb * wn rows for one

@@ -121,6 +121,32 @@ def test_rows_and_ragged_n(env, m):
         run_case(env, p, split_k=s)
 
 
+# Every kernel variant of the library (rows-per-wave blocks, waves along
+# rows, waves along K, load depth), forced through the MXG_TILE override.
+TILES = ["1,1,4,4", "1,1,8,4", "1,1,16,4", "1,4,1,16", "1,4,1,8", "1,7,1,8", "1,2,2,8",
+         "1,4,2,8", "2,1,4,4", "1,8,1,8", "2,2,2,4", "1,7,1,16"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_every_tile_variant(env, tile, monkeypatch):
+    """Each variant on a ragged N at every split, with 1, 5 and 8 tokens and
+    K slices down to one 128-wide block (waves along K left without work)."""
+    mx, _ = env
+    from workloads import generate
+
+    monkeypatch.setenv("MXG_TILE", tile)
+    ran = 0
+    for m, k in [(1, 2048), (5, 1024), (8, 2048)]:
+        for s in [1, 2, 4, 8]:
+            p = generate.random_problem(7000 + 10 * m + s, m, 1000, k, s)
+            try:
+                run_case(env, p, split_k=s, calls=2)
+                ran += 1
+            except mx.MxgUnsupported:
+                _say(f"tile {tile} unsupported at m={m} k={k} split_k={s}")
+    assert ran >= 6
+
+
 def test_single_nonzero_sweep(env):
     """One nonzero W element and one nonzero x element at swept positions: the
     result is one exact product, so any slip of the MFMA lane, K-piece or
