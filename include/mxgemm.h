@@ -61,13 +61,21 @@ extern "C" {
 #define MXG_STATE_COLLECT_ARR 2
 #define MXG_STATE_ERROR 3
 
-/* Split-K workspace header (uint32 words at the start of the workspace).
+/* Split-K workspace layout:
+ *   [0, 256)             header, uint32 words: EPOCH, (reserved), ERROR
+ *   [256, 256 + 8192)    one uint32 per workgroup: the epoch it read
+ *   [256 + 8192, ...)    (value, tag) pairs, see mxgemm_workspace_bytes
  * EPOCH tags every (value, tag) pair a GEMM call exchanges between its
  * workgroups (sync page, Mailbox docstring: a launch tags its hand-offs with
- * its epoch, so a pair from an earlier call never carries a live tag). */
+ * its epoch, so a pair from an earlier call never carries a live tag). Each
+ * workgroup stores the epoch it read into its own word; once workgroup 0
+ * has seen every word of the launch hold the epoch, it stores the next one
+ * (skipping 0), so the next call, and no workgroup of this one, reads it. A
+ * split-K launch has at most MXG_WS_MAX_GROUPS workgroups. */
 #define MXG_WS_HEADER_BYTES 256
+#define MXG_WS_FLAG_BYTES 8192
+#define MXG_WS_MAX_GROUPS 2048
 #define MXG_WS_EPOCH 0
-#define MXG_WS_ARRIVALS 1
 #define MXG_WS_ERROR 2
 
 #define MXG_ERR_COLLECT_SPIN 0x1u /* a collect gave up polling a slot */
@@ -97,11 +105,12 @@ int mailbox_init(mxg_mailbox* mb, void* slots, uint32_t* state, int32_t ranks,
                  int32_t rank, int64_t capacity_bytes, void* stream);
 
 /* Bytes of split-K workspace mxgemm_publish needs for these sizes: 0 when
- * split_k == 1, else MXG_WS_HEADER_BYTES + split_k * 64 * ceil(n/8)*8: eight
- * (value, tag) pairs of 8 bytes for each of 8 token rows and n/8 packs. */
+ * split_k == 1, else MXG_WS_HEADER_BYTES + MXG_WS_FLAG_BYTES
+ * + split_k * 64 * ceil(n/8)*8: eight (value, tag) pairs of 8 bytes for each
+ * of 8 token rows and n/8 packs. */
 size_t mxgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t split_k);
 
-/* Arm a workspace: zero every pair, EPOCH = 1, ARRIVALS = ERROR = 0. Call it
+/* Arm a workspace: zero every word, then EPOCH = 1. Call it
  * once before first use, outside capture; a workspace may then serve calls
  * of any size up to its capacity, in any order. Errors: MXG_EINVAL,
  * MXG_EALIGN, MXG_EHIP. */

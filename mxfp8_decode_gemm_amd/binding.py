@@ -33,7 +33,9 @@ MAX_ROWS = 8
 STATE_WORDS = 8
 STATE_NEXT, STATE_ACTIVE, STATE_COLLECT_ARR, STATE_ERROR = 0, 1, 2, 3
 WS_HEADER_BYTES = 256
-WS_EPOCH, WS_ARRIVALS, WS_ERROR = 0, 1, 2
+WS_FLAG_BYTES = 8192
+WS_MAX_GROUPS = 2048
+WS_EPOCH, WS_ERROR = 0, 2
 ERR_COLLECT_SPIN = 0x1
 ERR_SPLITK_SPIN = 0x2
 

@@ -22,9 +22,14 @@ LIB = os.path.join(LIBDIR, "libmxgemm.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no packed FP32 VALU instructions in any kernel.
+# atomic optimizer off: it rewrites a one-lane counter atomic into a wave
+# scan whose result is waited for at once, which would hold the workgroup
+# for a device-scope round trip where the count's result is needed only at
+# the end of the kernel.
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

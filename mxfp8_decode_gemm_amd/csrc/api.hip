@@ -63,8 +63,8 @@ size_t mxgemm_workspace_bytes(int32_t m, int32_t n, int32_t k, int32_t split_k) 
   (void)k;
   if (split_k <= 1 || n <= 0) return 0;
   const size_t n8 = (size_t)((n + 7) / 8) * 8;
-  // pairs[split][token 0..7][n / 8][8] of 8 bytes
-  return MXG_WS_HEADER_BYTES + (size_t)split_k * 8 * n8 * 8;
+  // header, per-workgroup epoch words, pairs[split][token 0..7][n / 8][8] of 8 bytes
+  return MXG_WS_HEADER_BYTES + MXG_WS_FLAG_BYTES + (size_t)split_k * 8 * n8 * 8;
 }
 
 size_t mxgemm_packed_weight_bytes(int32_t n, int32_t k) {
@@ -88,7 +88,8 @@ int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int3
 }
 
 int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
-  if (!workspace || workspace_bytes < MXG_WS_HEADER_BYTES || workspace_bytes % 16)
+  if (!workspace || workspace_bytes < MXG_WS_HEADER_BYTES + MXG_WS_FLAG_BYTES ||
+      workspace_bytes % 16)
     return MXG_EINVAL;
   if (!aligned16(workspace)) return MXG_EALIGN;
   return hip_code(launch_workspace_init(static_cast<uint32_t*>(workspace), workspace_bytes,
@@ -129,10 +130,13 @@ int publish_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale
   a.gen_stride = (int64_t)mb->ranks * mb->capacity_bytes;
   a.state = mb->state;
   a.ws_hdr = split_k > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.flags = split_k > 1 ? static_cast<uint32_t*>(workspace) + MXG_WS_HEADER_BYTES / 4 : nullptr;
   a.pairs = split_k > 1 ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
-                                                       MXG_WS_HEADER_BYTES)
+                                                       MXG_WS_HEADER_BYTES + MXG_WS_FLAG_BYTES)
                         : nullptr;
-  a.pairs_bytes = split_k > 1 ? (int64_t)(workspace_bytes - MXG_WS_HEADER_BYTES) : 0;
+  a.pairs_bytes = split_k > 1 ? (int64_t)(workspace_bytes - MXG_WS_HEADER_BYTES -
+                                          MXG_WS_FLAG_BYTES)
+                              : 0;
   a.xcd_groups = 0;
   a.c_out = c_out;
   a.m = m;

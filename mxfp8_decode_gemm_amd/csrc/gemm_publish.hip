@@ -230,17 +230,25 @@ __global__ void pack_weight_kernel(const uint8_t* w, const uint8_t* ws, int n, i
 
 // At least two waves per SIMD (<= 256 VGPRs): with split-K the grid must be
 // resident at once, and a second wave hides the other's conversion work.
+// With split-K one more wave, the control wave, runs beside the WN x WK
+// worker waves and does the call's bookkeeping while they stream: it reads
+// the generation and epoch, stores the epoch into this workgroup's word, and
+// in workgroup 0 advances the epoch once every workgroup has read it. No
+// worker wave waits for these round trips (loads and stores complete in
+// order per wave, so one in flight would hold the worker's W loads).
 template <int RB, int WN, int WK, int D, int SK>
-__global__ void __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(2)))
-gemm_publish_kernel(GemmArgs a) {
+__global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
+    __attribute__((amdgpu_waves_per_eu(2))) gemm_publish_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr int NT = 64 * WN * WK;
+  constexpr int NT = 64 * WN * WK;  // worker threads
   constexpr int RBT = RB * WN;    // 16-row blocks per tile
   constexpr int NTILE = 16 * RBT; // rows per tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const bool ctl = tid >= NT;           // the control wave (split-K only)
+  const int hand_tid = SK > 1 ? NT : 0; // reads the hand-off words
   const int wn = wave % WN;
   const int wk = wave / WN;
   const int r16 = lane & 15;  // A row / B column of this lane
@@ -265,7 +273,7 @@ gemm_publish_kernel(GemmArgs a) {
   const int NB = KS >> 7;           // 128-wide K blocks in the slice
   const int kb_lo = (wk * NB) / WK; // this wave's K blocks
   const int kb_hi = ((wk + 1) * NB) / WK;
-  const int nbw = kb_hi - kb_lo;
+  const int nbw = ctl ? 0 : kb_hi - kb_lo;  // the control wave streams nothing
   const int row0 = tile * NTILE;
   const size_t kslice0 = (size_t)slice * KS;
 
@@ -278,7 +286,7 @@ gemm_publish_kernel(GemmArgs a) {
   // _AllGatherKernel.kernel: the last CTA to arrive advances the state). The
   // loads are issued here and waited for only where the values are needed.
   uint32_t gen = 0, epoch = 0;
-  if (tid == 0) {
+  if (tid == hand_tid) {
     gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
     if (S > 1) epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH);
   }
@@ -289,8 +297,10 @@ gemm_publish_kernel(GemmArgs a) {
   const int wpr = KS >> 7;  // x-scale words per token row in the slice
   const int nsw = m * wpr;
   XStage<NT> xst;
-  xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
-  xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
+  if (!ctl) {
+    xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
+    xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
+  }
 
   // ---- W stream prologue (packed tiles, see mxgemm_pack_weight) ---------
   // Tile (rb, kb) is 2048 contiguous bytes: lane l's K pieces at 16 l and
@@ -326,22 +336,57 @@ gemm_publish_kernel(GemmArgs a) {
   };
   constexpr int G = D > 16 ? D : 16;  // K blocks per straight-line group
   const int ng0 = nbw < G ? nbw : G;
+  if (!ctl) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_w(d, d < ng0 ? d : -1);
+    for (int d = 0; d < D; ++d) load_w(d, d < ng0 ? d : -1);
 
-  // ---- x and its scales into LDS ---------------------------------------
-  // The x loads were issued first, so waiting for them leaves the W prologue
-  // in flight: the W stream starts at once and x lands in one round trip.
-  uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
-  xst.store(xl);
-  xst.store_scales(xsw);
-  if (xch > XStage<NT>::kChunks * NT || nsw > XStage<NT>::kWords * NT)
-    stage_rest<NT>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
-  if (tid == 0) {
+    // ---- x and its scales into LDS -------------------------------------
+    // The x loads were issued first, so waiting for them leaves the W
+    // prologue in flight: the W stream starts at once and x lands in one
+    // round trip.
+    uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
+    xst.store(xl);
+    xst.store_scales(xsw);
+    if (xch > XStage<NT>::kChunks * NT || nsw > XStage<NT>::kWords * NT)
+      stage_rest<NT>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
+  }
+  if (S == 1 && tid == hand_tid) {
     hdr[0] = gen;
     hdr[1] = epoch;
   }
   __syncthreads();
+
+  // ---- control wave: epoch bookkeeping while the workers stream ---------
+  if (S > 1 && ctl) {
+    if (tid == hand_tid) {
+      hdr[0] = gen;
+      hdr[1] = epoch;
+      // This workgroup has read the epoch (the stored word is the value
+      // read, so the store is issued after the load returned).
+      st_agent_u32(a.flags + blockIdx.x, epoch);
+    }
+    if (blockIdx.x == 0) {
+      // Every workgroup's word holding this call's epoch means every
+      // workgroup has read it: only then may the next epoch be stored.
+      const uint32_t e = __shfl(epoch, 0, 64);
+      uint32_t polls = 0;
+      bool ok = true;
+      for (;;) {
+        bool pending = false;
+        for (int i = lane; i < (int)gridDim.x; i += 64) pending |= ld_agent_u32(a.flags + i) != e;
+        if (!__any(pending)) break;
+        if (++polls >= a.spin_limit) {
+          ok = false;
+          if (lane == 0)
+            __hip_atomic_fetch_or(a.ws_hdr + MXG_WS_ERROR, MXG_ERR_SPLITK_SPIN, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (ok && lane == 0) st_agent_u32(a.ws_hdr + MXG_WS_EPOCH, e + 1u == 0u ? 1u : e + 1u);
+    }
+  }
 
   // ---- main loop: K blocks of this wave ---------------------------------
   v4f acc[RB];
@@ -423,23 +468,12 @@ gemm_publish_kernel(GemmArgs a) {
     pw = pw < 1 ? 1 : (pw > NW - 1 ? NW - 1 : pw);
   }
   const bool poller = wave < pw;
-  const bool sender = SK > 1 && (NW == 1 || wave >= pw);
-  const int counter_tid = NW > 1 ? NT - 64 : 0;  // first lane of the last wave
-
-  // Count this workgroup. Its epoch load returned before the LDS header was
-  // written, so it was performed before this count is issued; the count's
-  // result is needed only at the end, and it is issued by a wave that never
-  // polls, so its round trip delays no poll. (A release here would write
-  // back the whole L2 per workgroup.)
-  uint32_t arrived = 0;
-  if (S > 1 && tid == counter_tid)
-    arrived = __hip_atomic_fetch_add(a.ws_hdr + MXG_WS_ARRIVALS, 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+  const bool sender = SK > 1 && !ctl && (NW == 1 || wave >= pw);
 
   // ---- partial tile -> LDS [wk][t][row], summed over waves in K order ---
   __syncthreads();  // every wave is done with x in LDS
   float* red = reinterpret_cast<float*>(lds + kHeaderBytes);
-  if (tok) {
+  if (tok && !ctl) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int rl = (wn * RB + i) * 16 + 4 * grp;
@@ -548,16 +582,7 @@ gemm_publish_kernel(GemmArgs a) {
 
   // Hand the generation to the consumer once per grid (publishing_gemm page,
   // epilog_warp: block 0, one thread, sets the active stage word).
-  if (blockIdx.x == 0 && tid == 0) st_agent_u32(a.state + MXG_STATE_ACTIVE, gen);
-  if (S > 1 && tid == counter_tid && arrived == gridDim.x - 1u) {
-    // Last workgroup to arrive: every other count was performed before this
-    // one returned grid - 1, and each followed its workgroup's completed
-    // epoch load; this store is issued after that return. So the next
-    // launch, and no workgroup of this one, sees the next epoch (never 0).
-    const uint32_t next = epoch + 1u == 0u ? 1u : epoch + 1u;
-    st_agent_u32(a.ws_hdr + MXG_WS_ARRIVALS, 0u);
-    st_agent_u32(a.ws_hdr + MXG_WS_EPOCH, next);
-  }
+  if (blockIdx.x == 0 && tid == hand_tid) st_agent_u32(a.state + MXG_STATE_ACTIVE, gen);
 }
 
 // ---- variant table --------------------------------------------------------
@@ -575,7 +600,7 @@ struct Variant {
       MXG_V(RB, WN, WK, D, 8)
 
 const Variant kVariants[] = {
-    MXG_VARIANT(1, 1, 4, 4),  MXG_VARIANT(1, 1, 8, 4),  MXG_VARIANT(1, 1, 16, 4),
+    MXG_VARIANT(1, 1, 4, 4),  MXG_VARIANT(1, 1, 8, 4),  MXG_V(1, 1, 16, 4, 1),
     MXG_VARIANT(1, 4, 1, 16), MXG_VARIANT(1, 4, 1, 8),  MXG_VARIANT(1, 7, 1, 8),
     MXG_VARIANT(1, 2, 2, 8),  MXG_VARIANT(1, 4, 2, 8),  MXG_VARIANT(2, 1, 4, 4),
     MXG_VARIANT(1, 8, 1, 8),  MXG_VARIANT(2, 2, 2, 4),  MXG_VARIANT(1, 7, 1, 16),
@@ -608,7 +633,7 @@ bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
     // resident all at once.
     const long tiles = (n + tile_rows(c) - 1) / tile_rows(c);
     const long resident = gemm_resident_blocks(c, split_k, gemm_lds_bytes(c, m, ks));
-    return resident > 0 && tiles * split_k <= resident;
+    return resident > 0 && tiles * split_k <= resident && tiles * split_k <= MXG_WS_MAX_GROUPS;
   };
   if (const char* env = std::getenv("MXG_TILE")) {
     // Measurement override: exactly this variant, or no launch at all.
@@ -665,8 +690,8 @@ long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes) {
       hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
           hipSuccess)
     return -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->fn, tile_threads(c), lds_bytes) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->fn, tile_threads(c, split_k),
+                                                   lds_bytes) != hipSuccess)
     return -1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return -1;
@@ -690,7 +715,7 @@ hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t 
   const Variant* v = find_variant(c, a.split_k);
   if (!v) return hipErrorInvalidValue;
   const int tiles = (a.n + tile_rows(c) - 1) / tile_rows(c);
-  const dim3 grid(tiles * a.split_k), block(tile_threads(c));
+  const dim3 grid(tiles * a.split_k), block(tile_threads(c, a.split_k));
   const size_t lds = gemm_lds_bytes(c, a.m, a.k / a.split_k);
   GemmArgs args = a;
   args.xcd_groups = a.split_k > 1 && tiles % 8 == 0 ? 1 : 0;

@@ -82,39 +82,57 @@ __global__ void publish_kernel(uint8_t* slot, int64_t gen_stride, uint32_t* stat
   if (blockIdx.x == 0 && threadIdx.x == 0) st_agent_u32(state + MXG_STATE_ACTIVE, gen);
 }
 
-// Collect: one thread per (rank, pack), grid-stride.
+// Collect: one thread per (rank, pack), grid-stride. Every thread loads the
+// generation word together with its first pack in all three generations, so
+// when the payload is already there (the usual case) the collect costs one
+// round trip. Each workgroup counts itself once after its generation load has
+// returned (the count's operand depends on the loaded word); the last one to
+// arrive advances the generation at its end (all_gather page, step 3). No
+// workgroup of this launch can read the advanced value: every read returned
+// before its workgroup's count, and the advancing store follows the last one.
 __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capacity, int ranks,
                                uint32_t* state, uint8_t* out, int64_t nbytes,
                                uint32_t spin_limit) {
-  __shared__ uint32_t shared_gen;
-  if (threadIdx.x == 0) {
-    // Read the generation once, then count this workgroup; the last one to
-    // arrive advances the generation (all_gather page, step 3).
-    const uint32_t g = ld_agent_u32(state + MXG_STATE_NEXT) % MXG_GENERATIONS;
-    shared_gen = g;
-    const uint32_t before = __hip_atomic_fetch_add(state + MXG_STATE_COLLECT_ARR, 1u,
-                                                   __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (before == gridDim.x - 1u) {
-      st_agent_u32(state + MXG_STATE_COLLECT_ARR, 0u);
-      st_agent_u32(state + MXG_STATE_NEXT, (g + 1u) % MXG_GENERATIONS);
-    }
-  }
-  __syncthreads();
-  const uint32_t gen = shared_gen;
   const int64_t packs = nbytes / MXG_PACK_BYTES;
   const int64_t total = packs * ranks;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t graw = ld_agent_u32(state + MXG_STATE_NEXT);
+  uint64_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0, lo2 = 0, hi2 = 0;
+  if (i0 < total) {
+    const int64_t r = i0 / packs;
+    const uint64_t* s0 = reinterpret_cast<const uint64_t*>(
+        slots + r * capacity + (i0 - r * packs) * MXG_PACK_BYTES);
+    const int64_t gs = gen_stride / 8;
+    lo0 = ld_agent_u64(s0);
+    hi0 = ld_agent_u64(s0 + 1);
+    lo1 = ld_agent_u64(s0 + gs);
+    hi1 = ld_agent_u64(s0 + gs + 1);
+    lo2 = ld_agent_u64(s0 + 2 * gs);
+    hi2 = ld_agent_u64(s0 + 2 * gs + 1);
+  }
+  const uint32_t gen = graw % MXG_GENERATIONS;
+  uint32_t arrived = 0;
+  if (threadIdx.x == 0)
+    arrived = __hip_atomic_fetch_add(state + MXG_STATE_COLLECT_ARR,
+                                     1u + (graw == 0xFFFFFFFFu ? 1u : 0u), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
   uint8_t* base = slots + (size_t)gen * gen_stride;
   bool timed_out = false;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+  for (int64_t i = i0; i < total; i += stride) {
     const int64_t r = i / packs;
     const int64_t p = i - r * packs;
     uint64_t* slot = reinterpret_cast<uint64_t*>(base + r * capacity + p * MXG_PACK_BYTES);
     uint64_t lo, hi;
-    uint32_t polls = 0;
-    for (;;) {
+    if (i == i0) {
+      lo = gen == 0 ? lo0 : (gen == 1 ? lo1 : lo2);
+      hi = gen == 0 ? hi0 : (gen == 1 ? hi1 : hi2);
+    } else {
       lo = ld_agent_u64(slot);
       hi = ld_agent_u64(slot + 1);
+    }
+    uint32_t polls = 0;
+    for (;;) {
       const bool dirty = (uint32_t)lo == MXG_SENTINEL || (uint32_t)(lo >> 32) == MXG_SENTINEL ||
                          (uint32_t)hi == MXG_SENTINEL || (uint32_t)(hi >> 32) == MXG_SENTINEL;
       if (!dirty) break;
@@ -123,6 +141,8 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
         break;
       }
       __builtin_amdgcn_s_sleep(1);
+      lo = ld_agent_u64(slot);
+      hi = ld_agent_u64(slot + 1);
     }
     uint4 v;
     v.x = (uint32_t)lo;
@@ -136,6 +156,10 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
   if (timed_out)
     __hip_atomic_fetch_or(state + MXG_STATE_ERROR, MXG_ERR_COLLECT_SPIN, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0 && arrived == gridDim.x - 1u) {
+    st_agent_u32(state + MXG_STATE_COLLECT_ARR, 0u);
+    st_agent_u32(state + MXG_STATE_NEXT, (gen + 1u) % MXG_GENERATIONS);
+  }
 }
 
 unsigned blocks_for(int64_t items) {

@@ -18,6 +18,7 @@ struct GemmArgs {
   int64_t gen_stride; // bytes between generations: ranks * capacity
   uint32_t* state;    // mailbox state words
   uint32_t* ws_hdr;   // split-K workspace header (null when split_k == 1)
+  uint32_t* flags;    // split-K per-workgroup epoch words (null when split_k == 1)
   uint64_t* pairs;    // split-K (value, epoch) pairs (null when split_k == 1)
   int64_t pairs_bytes; // bytes of the pairs region
   uint16_t* c_out;    // raw BF16 output or null
@@ -34,7 +35,10 @@ struct TileCfg {
 };
 
 inline int tile_rows(const TileCfg& c) { return 16 * c.rb * c.wn; }
-inline int tile_threads(const TileCfg& c) { return 64 * c.wn * c.wk; }
+// Worker waves, plus the control wave of split-K launches.
+inline int tile_threads(const TileCfg& c, int split_k) {
+  return 64 * (c.wn * c.wk + (split_k > 1 ? 1 : 0));
+}
 
 // Dynamic LDS bytes of a launch (x slice, its scales, the partial tile).
 size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice);

@@ -59,7 +59,7 @@ class Workspace:
 
     def __init__(self, n: int, split_k: int, device=None, stream=None) -> None:
         self.nbytes = max(mx.mxgemm_workspace_bytes(8, n, 128 * split_k, split_k),
-                          mx.WS_HEADER_BYTES)
+                          mx.WS_HEADER_BYTES + mx.WS_FLAG_BYTES)
         self.buf = torch.empty(self.nbytes // 4, dtype=torch.int32, device=_dev(device))
         mx.mxgemm_workspace_init(self.buf, self.nbytes, stream)
 

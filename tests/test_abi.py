@@ -44,7 +44,7 @@ def test_sizes(mx):
     assert mx.mxg_mailbox_slots_bytes(9, 64) == 0
     assert mx.mxg_mailbox_slots_bytes(1, 24) == 0
     assert mx.mxgemm_workspace_bytes(8, 7168, 8192, 1) == 0
-    assert mx.mxgemm_workspace_bytes(8, 7168, 8192, 4) == 256 + 4 * 64 * 7168
+    assert mx.mxgemm_workspace_bytes(8, 7168, 8192, 4) == 256 + 8192 + 4 * 64 * 7168
 
 
 def _mb(mx, slots=256, state=512, ranks=1, rank=0, cap=512):
@@ -121,4 +121,5 @@ def test_misc(mx):
     assert lib.mxg_graph_launch(None, None) == -1
     assert lib.mxg_graph_destroy(None) == -1
     assert lib.mxgemm_workspace_init(None, 1024, None) == -1
-    assert lib.mxgemm_workspace_init(4100, 1024, None) == -2
+    assert lib.mxgemm_workspace_init(4096, 1024, None) == -1  # below header + epoch words
+    assert lib.mxgemm_workspace_init(4100, 8448, None) == -2

