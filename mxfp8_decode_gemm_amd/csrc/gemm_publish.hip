@@ -600,10 +600,11 @@ struct Variant {
       MXG_V(RB, WN, WK, D, 8)
 
 const Variant kVariants[] = {
-    MXG_VARIANT(1, 1, 4, 4),  MXG_VARIANT(1, 1, 8, 4),  MXG_V(1, 1, 16, 4, 1),
-    MXG_VARIANT(1, 4, 1, 16), MXG_VARIANT(1, 4, 1, 8),  MXG_VARIANT(1, 7, 1, 8),
-    MXG_VARIANT(1, 2, 2, 8),  MXG_VARIANT(1, 4, 2, 8),  MXG_VARIANT(2, 1, 4, 4),
-    MXG_VARIANT(1, 8, 1, 8),  MXG_VARIANT(2, 2, 2, 4),  MXG_VARIANT(1, 7, 1, 16),
+    MXG_VARIANT(1, 1, 4, 4), MXG_VARIANT(1, 1, 8, 4), MXG_V(1, 1, 16, 4, 1),
+    MXG_VARIANT(1, 4, 1, 8), MXG_VARIANT(1, 4, 1, 3), MXG_VARIANT(1, 7, 1, 8),
+    MXG_VARIANT(1, 7, 1, 4), MXG_VARIANT(1, 7, 1, 3), MXG_VARIANT(1, 2, 2, 8),
+    MXG_VARIANT(1, 4, 2, 8), MXG_VARIANT(2, 1, 4, 4), MXG_VARIANT(1, 8, 1, 8),
+    MXG_VARIANT(2, 2, 2, 4),
 };
 
 const Variant* find_variant(const TileCfg& c, int split_k) {
@@ -647,8 +648,11 @@ bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
   // tiles wide enough to reuse the staged x, and (with split-K) a grid that
   // is resident at once.
   const int nb = ks / 128;
-  static const TileCfg kSplit[] = {{1, 7, 1, 8}, {1, 4, 1, 8}, {1, 4, 1, 16}, {1, 4, 2, 8},
-                                   {2, 1, 4, 4}, {1, 1, 4, 4}};
+  // A shallow ring (3 K blocks of W per wave in flight) streams faster than a
+  // deep one: with the whole chip's loads queued at once, fewer per wave keep
+  // the workgroups' progress even (measured on N=7168, K=8192, m=8, S=4).
+  static const TileCfg kSplit[] = {{1, 7, 1, 3}, {1, 7, 1, 4}, {1, 4, 1, 3}, {1, 7, 1, 8},
+                                   {1, 4, 1, 8}, {1, 4, 2, 8}, {2, 1, 4, 4}, {1, 1, 4, 4}};
   static const TileCfg kLongK[] = {{1, 1, 16, 4}, {1, 1, 8, 8}, {1, 1, 8, 4}, {1, 1, 4, 4}};
   static const TileCfg kShortK[] = {{1, 1, 4, 4}, {1, 1, 8, 4}, {2, 1, 4, 4}};
   const TileCfg* list;

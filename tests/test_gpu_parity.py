@@ -122,8 +122,8 @@ def test_rows_and_ragged_n(env, m):
 
 # Every kernel variant of the library (rows-per-wave blocks, waves along
 # rows, waves along K, load depth), forced through the MXG_TILE override.
-TILES = ["1,1,4,4", "1,1,8,4", "1,1,16,4", "1,4,1,16", "1,4,1,8", "1,7,1,8", "1,2,2,8",
-         "1,4,2,8", "2,1,4,4", "1,8,1,8", "2,2,2,4", "1,7,1,16"]
+TILES = ["1,1,4,4", "1,1,8,4", "1,1,16,4", "1,4,1,8", "1,4,1,3", "1,7,1,8", "1,7,1,4",
+         "1,7,1,3", "1,2,2,8", "1,4,2,8", "2,1,4,4", "1,8,1,8", "2,2,2,4"]
 
 
 @pytest.mark.parametrize("tile", TILES)
