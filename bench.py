@@ -129,8 +129,9 @@ def cpu_baseline(problem, calls: int) -> tuple[dict, object]:
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the multi-GPU exchange is design only)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the exchange "
+              "across GPUs is a design only, and the workload is one GPU's share",
+              file=sys.stderr)
         return 2
     import numpy as np
     import torch
