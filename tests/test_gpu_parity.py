@@ -413,3 +413,95 @@ def test_pack_weight_layout(env, n, k):
                     sexp[(t * 16 + r) * 4:(t * 16 + r) * 4 + 4] = ws[row, kb * 4:kb * 4 + 4]
     assert np.array_equal(wp, expect)
     assert np.array_equal(wsp, sexp)
+
+
+def test_config4_million_alternating_calls(env):
+    """Config 4 at full count: 10^6 alternating-size calls (GEMM+publish into
+    slot 0, three emulated peers, collect) through one mailbox and one
+    workspace, in HIP graphs of 1000 calls replayed 1000 times. Every call's
+    collected words are compared on the device with the verified output of its
+    size, and sentinel words are counted; both counts must be 0, and the
+    mailbox is idle and the state words exact at the end. Only elementwise
+    torch ops with preallocated outputs run inside the graphs (no allocation,
+    no memset)."""
+    mx, dv = env
+    codecs, gemm, mailbox, tolerance = _oracle()
+    from workloads import generate
+
+    probs = [generate.config_problem(4, size=s) for s in (0, 1)]
+    ops = [dv.Operands(p) for p in probs]
+    peers = [generate.peer_payloads(p.seed, 4, p.m, p.n) for p in probs]
+    peer_dev = [[dv.upload(pp[r]) for r in range(3)] for pp in peers]
+    mbx = dv.Mailbox(4, 32768)
+    ws = dv.Workspace(7168, 4)
+    c_out = [torch.empty(p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
+    outs = [torch.empty(4 * p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
+    model = mailbox.MailboxModel(4, 32768)
+    stream = torch.cuda.Stream()
+
+    def call(s):
+        p = probs[s]
+        dv.publish(mbx, ops[s], 4, ws, c_out[s], stream=stream)
+        for r in range(1, 4):
+            mx.mailbox_publish(mbx.mb, r, peer_dev[s][r - 1], p.out_bytes, stream)
+        mx.mailbox_collect(mbx.mb, outs[s], p.out_bytes, stream)
+
+    # One verified call of each size: values against the oracle, mailbox bits
+    # against the oracle model.
+    expect = []
+    with torch.cuda.stream(stream):
+        for s, p in enumerate(probs):
+            call(s)
+            stream.synchronize()
+            raw = dv.as_u16(c_out[s]).reshape(p.m, p.n)
+            _, exact, abs_sum = gemm.gemm_publish_bits(p.w, p.ws, p.x, p.xs)
+            assert tolerance.within(raw, exact, abs_sum)
+            model.publish(0, raw)
+            for r in range(1, 4):
+                model.publish(r, peers[s][r - 1])
+            want = model.collect(p.out_bytes).reshape(4 * p.m, p.n)
+            assert np.array_equal(dv.as_u16(outs[s]).reshape(4 * p.m, p.n), want)
+            expect.append(torch.from_numpy(want.reshape(-1).view(np.int16).copy()).cuda())
+
+    words = [o.numel() // 2 for o in outs]
+    out32 = [o.view(torch.int32) for o in outs]
+    exp32 = [e.view(torch.int32) for e in expect]
+    mism = [torch.zeros(w, dtype=torch.int32, device="cuda") for w in words]
+    sent = [torch.zeros(w, dtype=torch.int32, device="cuda") for w in words]
+    m_ne = [torch.empty(w, dtype=torch.bool, device="cuda") for w in words]
+    m_se = [torch.empty(w, dtype=torch.bool, device="cuda") for w in words]
+    sentinel = -(2**31)  # 0x80000000 as int32
+
+    def call_and_check(s):
+        call(s)
+        torch.ne(out32[s], exp32[s], out=m_ne[s])
+        mism[s].add_(m_ne[s])
+        torch.eq(out32[s], sentinel, out=m_se[s])
+        sent[s].add_(m_se[s])
+
+    per_graph, replays = 1000, 1000
+    with torch.cuda.stream(stream):
+        for s in (0, 1):  # the checks once eagerly (warms every kernel)
+            call_and_check(s)
+        stream.synchronize()
+        mx.mxg_graph_begin(stream)
+        for i in range(per_graph):
+            call_and_check(i % 2)
+        g = mx.mxg_graph_end(stream)
+        for rep in range(replays):
+            mx.mxg_graph_launch(g, stream)
+            if rep % 100 == 99:
+                stream.synchronize()
+                _say(f"replays {rep + 1}/{replays}: "
+                     f"mismatched words {int(sum(int(t.sum()) for t in mism))}, "
+                     f"sentinel words {int(sum(int(t.sum()) for t in sent))}")
+        stream.synchronize()
+        mx.mxg_graph_destroy(g)
+    calls = 2 + 2 + per_graph * replays
+    assert sum(int(t.sum()) for t in mism) == 0
+    assert sum(int(t.sum()) for t in sent) == 0
+    assert not mailbox.check_idle_slots(mbx.slot_words())
+    st = mbx.state_words()
+    assert st[mx.STATE_NEXT] == calls % 3 and st[mx.STATE_ERROR] == 0
+    hdr = ws.header()
+    assert hdr[mx.WS_EPOCH] == 1 + calls and hdr[mx.WS_ERROR] == 0
