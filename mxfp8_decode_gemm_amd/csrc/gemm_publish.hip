@@ -625,7 +625,33 @@ size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice) {
 
 bool tile_available(const TileCfg& c) { return find_variant(c, 1) != nullptr; }
 
+static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out);
+
+// The choice depends only on the sizes and the device: remembered per key.
 bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
+  if (std::getenv("MXG_TILE")) return choose_tile_uncached(m, n, k, split_k, out);
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, int>, std::pair<bool, TileCfg>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  const auto key = std::make_tuple(dev, m, n, k, split_k);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      *out = it->second.second;
+      return it->second.first;
+    }
+  }
+  TileCfg c{};
+  const bool ok = choose_tile_uncached(m, n, k, split_k, &c);
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = std::make_pair(ok, c);
+  *out = c;
+  return ok;
+}
+
+static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out) {
   const int ks = k / split_k;
   auto fits = [&](const TileCfg& c) {
     if (!find_variant(c, split_k) || gemm_lds_bytes(c, m, ks) > 160 * 1024) return false;
@@ -644,36 +670,43 @@ bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
     *out = c;
     return true;
   }
-  // Preference order: enough waves per CU to keep tens of KB of W in flight,
-  // tiles wide enough to reuse the staged x, and (with split-K) a grid that
-  // is resident at once.
-  const int nb = ks / 128;
-  // A shallow ring (3 K blocks of W per wave in flight) streams faster than a
-  // deep one: with the whole chip's loads queued at once, fewer per wave keep
-  // the workgroups' progress even (measured on N=7168, K=8192, m=8, S=4).
-  static const TileCfg kSplit[] = {{1, 7, 1, 3}, {1, 7, 1, 4}, {1, 4, 1, 3}, {1, 7, 1, 8},
+  // Cost of a candidate: the W bytes one CU streams, plus a fixed cost per
+  // workgroup (x staging, exchange, publish), times the workgroups each CU
+  // runs. Lists are in preference order for ties; shallow rings (3 K blocks
+  // per wave) first, since they keep the workgroups' progress even when the
+  // whole chip's loads are queued at once. Fitted to sweeps of every variant
+  // on N=7168/K=8192/m=8/S=4, N=7168/K=2048/m=4, N=4096/K=16384 (m 1..8,
+  // S 1/4/8), N=7168/K=4096/m=1/S=4 and N=2048/K=8192/m=8/S=4.
+  static const TileCfg kSplit[] = {{1, 7, 1, 3}, {1, 4, 1, 3}, {1, 2, 2, 8}, {1, 7, 1, 4},
                                    {1, 4, 1, 8}, {1, 4, 2, 8}, {2, 1, 4, 4}, {1, 1, 4, 4}};
-  static const TileCfg kLongK[] = {{1, 1, 16, 4}, {1, 1, 8, 8}, {1, 1, 8, 4}, {1, 1, 4, 4}};
-  static const TileCfg kShortK[] = {{1, 1, 4, 4}, {1, 1, 8, 4}, {2, 1, 4, 4}};
-  const TileCfg* list;
-  size_t count;
-  if (split_k > 1) {
-    list = kSplit;
-    count = sizeof(kSplit) / sizeof(kSplit[0]);
-  } else if (nb >= 64) {
-    list = kLongK;
-    count = sizeof(kLongK) / sizeof(kLongK[0]);
-  } else {
-    list = kShortK;
-    count = sizeof(kShortK) / sizeof(kShortK[0]);
+  static const TileCfg kNoSplit[] = {{1, 1, 16, 4}, {1, 1, 8, 4}, {1, 2, 2, 8},
+                                     {1, 4, 1, 3}, {1, 1, 4, 4}, {2, 1, 4, 4}};
+  const TileCfg* list = split_k > 1 ? kSplit : kNoSplit;
+  const size_t count = split_k > 1 ? sizeof(kSplit) / sizeof(kSplit[0])
+                                   : sizeof(kNoSplit) / sizeof(kNoSplit[0]);
+  int cus = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (cus < 1) cus = 1;
   }
+  constexpr double kGroupCost = 32768.0;  // bytes-equivalent fixed cost per workgroup
+  bool found = false;
+  double best = 0.0;
   for (size_t i = 0; i < count; ++i) {
-    if (fits(list[i])) {
-      *out = list[i];
-      return true;
+    const TileCfg& c = list[i];
+    if (c.wk > ks / 128 || !fits(c)) continue;  // every wave along K gets a K block
+    const long grid = (long)((n + tile_rows(c) - 1) / tile_rows(c)) * split_k;
+    const long per_cu = (grid + cus - 1) / cus;
+    const double cost = (double)per_cu * ((double)tile_rows(c) * ks + kGroupCost);
+    if (!found || cost < best) {
+      best = cost;
+      *out = c;
+      found = true;
     }
   }
-  return false;
+  return found;
 }
 
 long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes) {
