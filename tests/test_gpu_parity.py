@@ -415,39 +415,38 @@ def test_pack_weight_layout(env, n, k):
     assert np.array_equal(wsp, sexp)
 
 
-def test_config4_million_alternating_calls(env):
-    """Config 4 at full count: 10^6 alternating-size calls (GEMM+publish into
-    slot 0, three emulated peers, collect) through one mailbox and one
-    workspace, in HIP graphs of 1000 calls replayed 1000 times. Every call's
-    collected words are compared on the device with the verified output of its
-    size, and sentinel words are counted; both counts must be 0, and the
-    mailbox is idle and the state words exact at the end. Only elementwise
-    torch ops with preallocated outputs run inside the graphs (no allocation,
-    no memset)."""
+def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=None):
+    """Calls cycling over `probs` (GEMM+publish into slot 0, emulated peers in
+    slots 1.., collect) through one mailbox and one workspace. The first call
+    of each problem is verified eagerly (values against the oracle, mailbox
+    bits against the oracle model); then `per_graph` calls are captured in one
+    HIP graph and replayed `replays` times, every call's collected words
+    compared on the device with the verified output of its problem and
+    sentinel words counted. Only elementwise torch ops with preallocated
+    outputs run inside the graph (no allocation, no memset)."""
     mx, dv = env
     codecs, gemm, mailbox, tolerance = _oracle()
     from workloads import generate
 
-    probs = [generate.config_problem(4, size=s) for s in (0, 1)]
     ops = [dv.Operands(p) for p in probs]
-    peers = [generate.peer_payloads(p.seed, 4, p.m, p.n) for p in probs]
-    peer_dev = [[dv.upload(pp[r]) for r in range(3)] for pp in peers]
-    mbx = dv.Mailbox(4, 32768)
-    ws = dv.Workspace(7168, 4)
+    peers = [generate.peer_payloads(p.seed, ranks, p.m, p.n) for p in probs]
+    peer_dev = [[dv.upload(pp[r]) for r in range(ranks - 1)] for pp in peers]
+    mbx = dv.Mailbox(ranks, capacity)
+    ws = dv.Workspace(ws_n or max(p.n for p in probs), split_k) if split_k > 1 else None
+    epoch0 = ws.header()[mx.WS_EPOCH] if ws is not None else 0
     c_out = [torch.empty(p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
-    outs = [torch.empty(4 * p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
-    model = mailbox.MailboxModel(4, 32768)
+    outs = [torch.empty(ranks * p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
+    model = mailbox.MailboxModel(ranks, capacity)
     stream = torch.cuda.Stream()
+    P = len(probs)
 
     def call(s):
         p = probs[s]
-        dv.publish(mbx, ops[s], 4, ws, c_out[s], stream=stream)
-        for r in range(1, 4):
+        dv.publish(mbx, ops[s], split_k, ws, c_out[s], stream=stream)
+        for r in range(1, ranks):
             mx.mailbox_publish(mbx.mb, r, peer_dev[s][r - 1], p.out_bytes, stream)
         mx.mailbox_collect(mbx.mb, outs[s], p.out_bytes, stream)
 
-    # One verified call of each size: values against the oracle, mailbox bits
-    # against the oracle model.
     expect = []
     with torch.cuda.stream(stream):
         for s, p in enumerate(probs):
@@ -455,12 +454,12 @@ def test_config4_million_alternating_calls(env):
             stream.synchronize()
             raw = dv.as_u16(c_out[s]).reshape(p.m, p.n)
             _, exact, abs_sum = gemm.gemm_publish_bits(p.w, p.ws, p.x, p.xs)
-            assert tolerance.within(raw, exact, abs_sum)
+            assert tolerance.within(raw, exact, abs_sum), p.name
             model.publish(0, raw)
-            for r in range(1, 4):
+            for r in range(1, ranks):
                 model.publish(r, peers[s][r - 1])
-            want = model.collect(p.out_bytes).reshape(4 * p.m, p.n)
-            assert np.array_equal(dv.as_u16(outs[s]).reshape(4 * p.m, p.n), want)
+            want = model.collect(p.out_bytes).reshape(ranks * p.m, p.n)
+            assert np.array_equal(dv.as_u16(outs[s]).reshape(ranks * p.m, p.n), want), p.name
             expect.append(torch.from_numpy(want.reshape(-1).view(np.int16).copy()).cuda())
 
     words = [o.numel() // 2 for o in outs]
@@ -479,29 +478,64 @@ def test_config4_million_alternating_calls(env):
         torch.eq(out32[s], sentinel, out=m_se[s])
         sent[s].add_(m_se[s])
 
-    per_graph, replays = 1000, 1000
+    def counts():
+        return (sum(int(t.sum()) for t in mism), sum(int(t.sum()) for t in sent))
+
     with torch.cuda.stream(stream):
-        for s in (0, 1):  # the checks once eagerly (warms every kernel)
+        for s in range(P):  # the checks once eagerly (warms every kernel)
             call_and_check(s)
         stream.synchronize()
         mx.mxg_graph_begin(stream)
         for i in range(per_graph):
-            call_and_check(i % 2)
+            call_and_check(i % P)
         g = mx.mxg_graph_end(stream)
         for rep in range(replays):
             mx.mxg_graph_launch(g, stream)
-            if rep % 100 == 99:
+            if replays >= 100 and rep % 100 == 99:
                 stream.synchronize()
-                _say(f"replays {rep + 1}/{replays}: "
-                     f"mismatched words {int(sum(int(t.sum()) for t in mism))}, "
-                     f"sentinel words {int(sum(int(t.sum()) for t in sent))}")
+                _say(f"replays {rep + 1}/{replays}: mismatched words {counts()[0]}, "
+                     f"sentinel words {counts()[1]}")
         stream.synchronize()
         mx.mxg_graph_destroy(g)
-    calls = 2 + 2 + per_graph * replays
-    assert sum(int(t.sum()) for t in mism) == 0
-    assert sum(int(t.sum()) for t in sent) == 0
+    calls = 2 * P + per_graph * replays
+    assert counts() == (0, 0)
     assert not mailbox.check_idle_slots(mbx.slot_words())
     st = mbx.state_words()
     assert st[mx.STATE_NEXT] == calls % 3 and st[mx.STATE_ERROR] == 0
-    hdr = ws.header()
-    assert hdr[mx.WS_EPOCH] == 1 + calls and hdr[mx.WS_ERROR] == 0
+    if ws is not None:
+        hdr = ws.header()
+        assert hdr[mx.WS_EPOCH] == epoch0 + calls and hdr[mx.WS_ERROR] == 0
+    return calls
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+@pytest.mark.parametrize("split_k", [1, 4, 8])
+def test_config3_graph_1000_calls(env, m, split_k):
+    """Config 3 as stated: 1000 back-to-back calls in one HIP graph, four
+    emulated rank slots, the three generations cycling."""
+    from workloads import generate
+
+    p = generate.config_problem(3, m=m, split_k=split_k)
+    graph_soak(env, [p], split_k, 4, 65536, per_graph=1000, replays=1)
+
+
+@pytest.mark.parametrize("dist", ["outliers", "normal"])
+def test_config2_graph_100_calls(env, dist):
+    """Config 2 as stated: the epoch advances once per call over 100
+    graph-captured calls, every output identical to the verified one."""
+    from workloads import generate
+
+    p = generate.config_problem(2, dist=dist)
+    graph_soak(env, [p], 4, 1, 114688, per_graph=100, replays=1)
+
+
+def test_config4_million_alternating_calls(env):
+    """Config 4 at full count: 10^6 alternating-size calls (GEMM+publish into
+    slot 0, three emulated peers, collect) through one mailbox and one
+    workspace, in HIP graphs of 1000 calls replayed 1000 times: zero
+    mismatched and zero sentinel words, the mailbox idle and the state words
+    exact at the end."""
+    from workloads import generate
+
+    probs = [generate.config_problem(4, size=s) for s in (0, 1)]
+    graph_soak(env, probs, 4, 4, 32768, per_graph=1000, replays=1000, ws_n=7168)
