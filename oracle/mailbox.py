@@ -26,6 +26,14 @@ of different sizes share one mailbox (the all_gather page's byte-capacity
 layout; the publishing_gemm page's fixed hidden-size stride is the other
 reading, not used).
 
+All-reduce consumer (publishing_gemm page, module docstring: the GEMM's
+published output is summed across ranks by the boundary all-reduce). The pages
+do not print its internals, so it is taken from the plain meaning of an
+all-reduce in FP32: ``collect_sum`` returns, for every BF16 position, the FP32
+sum of the rank slots' values taken in ascending rank order, rounded once to
+BF16 (nearest even); the mailbox is reset and advanced exactly as by
+``collect``.
+
 ``EpochModel`` models the split-K hand-off tag: it starts at 1, and every GEMM
 call that exchanges partials advances it by one, skipping 0 on wrap-around
 (sync page, ``Mailbox`` docstring: each launch tags its hand-offs with its
@@ -36,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import SENTINEL_U32, clear_negative_zero
+from .codecs import SENTINEL_U32, bf16_rne_bits, bf16_to_f64, clear_negative_zero
 
 GENERATIONS = 3  # all_gather page, module docstring: three generations
 PACK_BYTES = 16  # all_gather page: one thread a 16-byte pack
@@ -123,10 +131,31 @@ class MailboxModel:
         self.collects += 1
         return out
 
+    def collect_sum(self, nbytes: int) -> np.ndarray:
+        """Collect ``nbytes`` from every rank slot of the current generation
+        and return their all-reduce: [nbytes / 2] uint16 BF16 bits (see
+        ``allreduce_bf16``). Resets and advances like ``collect``."""
+        return allreduce_bf16(self.collect(nbytes))
+
     # -- invariants --------------------------------------------------------
     def idle(self) -> bool:
         """Every word of every generation is the sentinel."""
         return bool(np.all(self.slots == SENTINEL_U32))
+
+
+def allreduce_bf16(halves: np.ndarray) -> np.ndarray:
+    """All-reduce of R BF16 payloads, [R, H] uint16 -> [H] uint16: each
+    position's values are added in FP32 in ascending rank order (each addition
+    rounded to FP32, nearest even), and the FP32 total is rounded once to BF16
+    (nearest even)."""
+    h = np.asarray(halves, dtype=np.uint16)
+    if h.ndim != 2 or h.shape[0] < 1:
+        raise ValueError("expected [ranks, halves]")
+    vals = bf16_to_f64(h).astype(np.float32)  # BF16 -> FP32 is exact
+    acc = vals[0].copy()
+    for r in range(1, h.shape[0]):
+        acc = np.add(acc, vals[r], dtype=np.float32)
+    return bf16_rne_bits(acc.astype(np.float64))
 
 
 def check_collected(out_halves: np.ndarray) -> list[str]:
