@@ -209,6 +209,20 @@ int mailbox_publish(const mxg_mailbox* mb, int32_t rank, const void* src,
  * Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY, MXG_EHIP. */
 int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream);
 
+/* All-reduce collect: the consumer that sums the ranks' published outputs
+ * (publishing_gemm page, module docstring: the boundary all-reduce after the
+ * row-parallel GEMM). The pages do not print its internals; this is the plain
+ * meaning in FP32. For every pack p < nbytes/16 of generation g =
+ * state[NEXT], each rank's pack is polled as in mailbox_collect, the eight
+ * BF16 values at each position are added in FP32 in ascending rank order,
+ * and the sums are rounded once to BF16 (nearest even) into out + 16 p
+ * ([m, n] BF16 for an [m, n] payload; a sum can round to negative zero).
+ * Every rank's pack is reset to the sentinel and the generation advances as
+ * in mailbox_collect; a pack still holding a sentinel after the spin limit
+ * sets MXG_ERR_COLLECT_SPIN. `out` is device memory of nbytes bytes, 16-B
+ * aligned. Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY, MXG_EHIP. */
+int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream);
+
 /* Poll limit of the device spin loops (collect and split-K), in polls; the
  * loops back off with s_sleep between polls. Returns the previous limit.
  * A limit of 0 restores the default (2^20 polls). Process-wide. */

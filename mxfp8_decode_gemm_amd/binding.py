@@ -94,6 +94,7 @@ def _load() -> ctypes.CDLL:
                                                 sz, vp, vp, vp, vp]),
         "mailbox_publish": (ctypes.c_int, [mbp, i32, vp, i64, vp]),
         "mailbox_collect": (ctypes.c_int, [mbp, vp, i64, vp]),
+        "mailbox_collect_sum": (ctypes.c_int, [mbp, vp, i64, vp]),
         "mxg_set_spin_limit": (u32, [u32]),
         "mxg_graph_begin": (ctypes.c_int, [vp]),
         "mxg_graph_end": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
@@ -239,6 +240,11 @@ def mailbox_publish(mb: mxg_mailbox, rank: int, src, nbytes: int, stream=None) -
 def mailbox_collect(mb: mxg_mailbox, out, nbytes: int, stream=None) -> None:
     _check(_lib.mailbox_collect(ctypes.byref(mb), _ptr(out), nbytes, _stream(stream)),
            "mailbox_collect")
+
+
+def mailbox_collect_sum(mb: mxg_mailbox, out, nbytes: int, stream=None) -> None:
+    _check(_lib.mailbox_collect_sum(ctypes.byref(mb), _ptr(out), nbytes, _stream(stream)),
+           "mailbox_collect_sum")
 
 
 def mxg_set_spin_limit(polls: int) -> int:

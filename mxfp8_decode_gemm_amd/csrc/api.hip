@@ -190,6 +190,17 @@ int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stre
       spin_limit(), static_cast<hipStream_t>(stream)));
 }
 
+int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream) {
+  if (!mailbox_ok(mb) || !out) return MXG_EINVAL;
+  if (!aligned16(out) || !aligned16(mb->slots) || !aligned16(mb->state)) return MXG_EALIGN;
+  if (nbytes <= 0 || nbytes > mb->capacity_bytes || nbytes % MXG_PACK_BYTES)
+    return MXG_ECAPACITY;
+  return hip_code(launch_mailbox_collect_sum(
+      static_cast<uint8_t*>(mb->slots), (int64_t)mb->ranks * mb->capacity_bytes,
+      mb->capacity_bytes, mb->ranks, mb->state, static_cast<uint8_t*>(out), nbytes,
+      spin_limit(), static_cast<hipStream_t>(stream)));
+}
+
 uint32_t mxg_set_spin_limit(uint32_t polls) {
   return g_spin_limit.exchange(polls == 0 ? (1u << 20) : polls);
 }

@@ -162,6 +162,87 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
   }
 }
 
+// All-reduce collect: one thread per pack p < nbytes/16. Each rank's pack of
+// generation g is polled until none of its words is the sentinel (all
+// ranks' first loads issued together with the generation word), its eight
+// BF16 values are added in FP32 in ascending rank order, the sums are rounded
+// once to BF16 (nearest even) into out + 16 p, and every rank's pack is reset
+// to the sentinel. Generation hand-off and timeout as in collect_kernel.
+__global__ void collect_sum_kernel(uint8_t* slots, int64_t gen_stride, int64_t capacity,
+                                   int ranks, uint32_t* state, uint8_t* out, int64_t nbytes,
+                                   uint32_t spin_limit) {
+  const int64_t packs = nbytes / MXG_PACK_BYTES;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const uint32_t graw = ld_agent_u32(state + MXG_STATE_NEXT);
+  const uint32_t gen = graw % MXG_GENERATIONS;
+  uint32_t arrived = 0;
+  if (threadIdx.x == 0)
+    arrived = __hip_atomic_fetch_add(state + MXG_STATE_COLLECT_ARR,
+                                     1u + (graw == 0xFFFFFFFFu ? 1u : 0u), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+  uint8_t* base = slots + (size_t)gen * gen_stride;
+  bool timed_out = false;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < packs; p += stride) {
+    uint64_t lo[MXG_MAX_RANKS], hi[MXG_MAX_RANKS];
+#pragma unroll
+    for (int r = 0; r < MXG_MAX_RANKS; ++r) {
+      if (r < ranks) {
+        const uint64_t* s = reinterpret_cast<const uint64_t*>(base + r * capacity + p * MXG_PACK_BYTES);
+        lo[r] = ld_agent_u64(s);
+        hi[r] = ld_agent_u64(s + 1);
+      }
+    }
+    float acc[8];
+#pragma unroll
+    for (int r = 0; r < MXG_MAX_RANKS; ++r) {
+      if (r >= ranks) continue;
+      const uint64_t* s = reinterpret_cast<const uint64_t*>(base + r * capacity + p * MXG_PACK_BYTES);
+      uint32_t polls = 0;
+      for (;;) {
+        const bool dirty =
+            (uint32_t)lo[r] == MXG_SENTINEL || (uint32_t)(lo[r] >> 32) == MXG_SENTINEL ||
+            (uint32_t)hi[r] == MXG_SENTINEL || (uint32_t)(hi[r] >> 32) == MXG_SENTINEL;
+        if (!dirty) break;
+        if (++polls >= spin_limit) {
+          timed_out = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        lo[r] = ld_agent_u64(s);
+        hi[r] = ld_agent_u64(s + 1);
+      }
+      const uint32_t w[4] = {(uint32_t)lo[r], (uint32_t)(lo[r] >> 32), (uint32_t)hi[r],
+                             (uint32_t)(hi[r] >> 32)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t half = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const float v = __uint_as_float(half << 16);  // BF16 -> FP32 is exact
+        acc[e] = r == 0 ? v : acc[e] + v;
+      }
+    }
+    uint4 o;
+    uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const __bf16 a = (__bf16)acc[2 * q];
+      const __bf16 b = (__bf16)acc[2 * q + 1];
+      ow[q] = (uint32_t)__builtin_bit_cast(uint16_t, a) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    }
+    *reinterpret_cast<uint4*>(out + p * MXG_PACK_BYTES) = o;
+    for (int r = 0; r < ranks; ++r)
+      *reinterpret_cast<uint4*>(base + r * capacity + p * MXG_PACK_BYTES) =
+          uint4{MXG_SENTINEL, MXG_SENTINEL, MXG_SENTINEL, MXG_SENTINEL};
+  }
+  if (timed_out)
+    __hip_atomic_fetch_or(state + MXG_STATE_ERROR, MXG_ERR_COLLECT_SPIN, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0 && arrived == gridDim.x - 1u) {
+    st_agent_u32(state + MXG_STATE_COLLECT_ARR, 0u);
+    st_agent_u32(state + MXG_STATE_NEXT, (gen + 1u) % MXG_GENERATIONS);
+  }
+}
+
 unsigned blocks_for(int64_t items) {
   const int64_t b = (items + kThreads - 1) / kThreads;
   return (unsigned)(b < 1 ? 1 : (b > (int64_t)kMaxBlocks ? kMaxBlocks : b));
@@ -203,6 +284,15 @@ hipError_t launch_mailbox_collect(uint8_t* slots, int64_t gen_stride, int64_t ca
                                   uint32_t spin_limit, hipStream_t s) {
   const int64_t items = nbytes / MXG_PACK_BYTES * ranks;
   hipLaunchKernelGGL(collect_kernel, dim3(blocks_for(items)), dim3(kThreads), 0, s, slots,
+                     gen_stride, capacity, ranks, state, out, nbytes, spin_limit);
+  return hipGetLastError();
+}
+
+hipError_t launch_mailbox_collect_sum(uint8_t* slots, int64_t gen_stride, int64_t capacity,
+                                      int ranks, uint32_t* state, uint8_t* out, int64_t nbytes,
+                                      uint32_t spin_limit, hipStream_t s) {
+  const int64_t packs = nbytes / MXG_PACK_BYTES;
+  hipLaunchKernelGGL(collect_sum_kernel, dim3(blocks_for(packs)), dim3(kThreads), 0, s, slots,
                      gen_stride, capacity, ranks, state, out, nbytes, spin_limit);
   return hipGetLastError();
 }

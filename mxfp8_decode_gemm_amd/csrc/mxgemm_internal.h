@@ -71,6 +71,9 @@ hipError_t launch_mailbox_publish(uint8_t* slot, int64_t gen_stride, uint32_t* s
 hipError_t launch_mailbox_collect(uint8_t* slots, int64_t gen_stride, int64_t capacity,
                                   int ranks, uint32_t* state, uint8_t* out,
                                   int64_t nbytes, uint32_t spin_limit, hipStream_t s);
+hipError_t launch_mailbox_collect_sum(uint8_t* slots, int64_t gen_stride, int64_t capacity,
+                                      int ranks, uint32_t* state, uint8_t* out, int64_t nbytes,
+                                      uint32_t spin_limit, hipStream_t s);
 
 uint32_t spin_limit();
 

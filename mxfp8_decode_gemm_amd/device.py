@@ -104,6 +104,15 @@ def collect(mailbox: Mailbox, nbytes: int, out: torch.Tensor = None, stream=None
     return out
 
 
+def collect_sum(mailbox: Mailbox, nbytes: int, out: torch.Tensor = None,
+                stream=None) -> torch.Tensor:
+    """One mailbox_collect_sum; returns the [nbytes] byte all-reduce as uint16."""
+    if out is None:
+        out = torch.empty(nbytes // 2, dtype=torch.int16, device=mailbox.slots.device)
+    mx.mailbox_collect_sum(mailbox.mb, out, nbytes, stream)
+    return out
+
+
 def as_u16(t: torch.Tensor) -> np.ndarray:
     """uint16 host copy of a 16-bit device tensor."""
     return t.cpu().numpy().view(np.uint16).copy()

@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -95,9 +95,12 @@ def test_collect_and_publish_capacity(mx, nbytes, code):
     mb = _mb(mx)
     lib = mx.library()
     assert lib.mailbox_collect(ctypes.byref(mb), 4096, nbytes, None) == code
+    assert lib.mailbox_collect_sum(ctypes.byref(mb), 4096, nbytes, None) == code
     assert lib.mailbox_publish(ctypes.byref(mb), 0, 4096, nbytes, None) == code
     assert lib.mailbox_publish(ctypes.byref(mb), 1, 4096, 16, None) == -1
     assert lib.mailbox_collect(ctypes.byref(mb), 4100, 16, None) == -2
+    assert lib.mailbox_collect_sum(ctypes.byref(mb), 4100, 16, None) == -2
+    assert lib.mailbox_collect_sum(ctypes.byref(mb), None, 16, None) == -1
 
 
 def test_pack_sizes_and_validation(mx):

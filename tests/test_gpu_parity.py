@@ -415,15 +415,18 @@ def test_pack_weight_layout(env, n, k):
     assert np.array_equal(wsp, sexp)
 
 
-def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=None):
+def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=None,
+               mode="gather"):
     """Calls cycling over `probs` (GEMM+publish into slot 0, emulated peers in
     slots 1.., collect) through one mailbox and one workspace. The first call
     of each problem is verified eagerly (values against the oracle, mailbox
     bits against the oracle model); then `per_graph` calls are captured in one
     HIP graph and replayed `replays` times, every call's collected words
     compared on the device with the verified output of its problem and
-    sentinel words counted. Only elementwise torch ops with preallocated
-    outputs run inside the graph (no allocation, no memset)."""
+    sentinel words counted. mode "gather" collects rank-major
+    (mailbox_collect), "sum" all-reduces the slots (mailbox_collect_sum).
+    Only elementwise torch ops with preallocated outputs run inside the graph
+    (no allocation, no memset)."""
     mx, dv = env
     codecs, gemm, mailbox, tolerance = _oracle()
     from workloads import generate
@@ -435,7 +438,8 @@ def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=No
     ws = dv.Workspace(ws_n or max(p.n for p in probs), split_k) if split_k > 1 else None
     epoch0 = ws.header()[mx.WS_EPOCH] if ws is not None else 0
     c_out = [torch.empty(p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
-    outs = [torch.empty(ranks * p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
+    rows = ranks if mode == "gather" else 1
+    outs = [torch.empty(rows * p.m * p.n, dtype=torch.int16, device="cuda") for p in probs]
     model = mailbox.MailboxModel(ranks, capacity)
     stream = torch.cuda.Stream()
     P = len(probs)
@@ -445,7 +449,10 @@ def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=No
         dv.publish(mbx, ops[s], split_k, ws, c_out[s], stream=stream)
         for r in range(1, ranks):
             mx.mailbox_publish(mbx.mb, r, peer_dev[s][r - 1], p.out_bytes, stream)
-        mx.mailbox_collect(mbx.mb, outs[s], p.out_bytes, stream)
+        if mode == "gather":
+            mx.mailbox_collect(mbx.mb, outs[s], p.out_bytes, stream)
+        else:
+            mx.mailbox_collect_sum(mbx.mb, outs[s], p.out_bytes, stream)
 
     expect = []
     with torch.cuda.stream(stream):
@@ -458,8 +465,11 @@ def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=No
             model.publish(0, raw)
             for r in range(1, ranks):
                 model.publish(r, peers[s][r - 1])
-            want = model.collect(p.out_bytes).reshape(ranks * p.m, p.n)
-            assert np.array_equal(dv.as_u16(outs[s]).reshape(ranks * p.m, p.n), want), p.name
+            if mode == "gather":
+                want = model.collect(p.out_bytes).reshape(rows * p.m, p.n)
+            else:
+                want = model.collect_sum(p.out_bytes).reshape(p.m, p.n)
+            assert np.array_equal(dv.as_u16(outs[s]).reshape(rows * p.m, p.n), want), p.name
             expect.append(torch.from_numpy(want.reshape(-1).view(np.int16).copy()).cuda())
 
     words = [o.numel() // 2 for o in outs]
