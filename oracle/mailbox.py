@@ -26,6 +26,13 @@ of different sizes share one mailbox (the all_gather page's byte-capacity
 layout; the publishing_gemm page's fixed hidden-size stride is the other
 reading, not used).
 
+Word payloads (all_gather page, module docstring, step 1, and
+``LamportAllGather.__call__``): the all-gather moves arbitrary 32-bit words,
+and a word equal to the sentinel is published as 0 (FP32 negative zero becomes
+positive zero); every other word is published unchanged. ``publish_words``
+models that publish, ``all_gather`` the fused call (publish the caller's own
+slot, then collect every slot).
+
 All-reduce consumer (publishing_gemm page, module docstring: the GEMM's
 published output is summed across ranks by the boundary all-reduce). The pages
 do not print its internals, so it is taken from the plain meaning of an
@@ -111,6 +118,27 @@ class MailboxModel:
         self.slots[g, rank, : nbytes // 4] = halves_to_words(clear_negative_zero(bits))
         self.active = g
 
+    def publish_words(self, rank: int, words: np.ndarray) -> None:
+        """Publish a payload of uint32 words into slot ``rank`` of the current
+        generation, each word equal to the sentinel replaced by 0."""
+        if not 0 <= rank < self.ranks:
+            raise ValueError("rank outside the mailbox")
+        w = np.asarray(words, dtype=np.uint32).reshape(-1)
+        nbytes = w.size * 4
+        if not accepts(nbytes, self.capacity_bytes):
+            raise ValueError(f"payload of {nbytes} bytes does not fit")
+        g = self.next
+        self.slots[g, rank, : w.size] = sanitize_words(w)
+        self.active = g
+
+    def all_gather(self, rank: int, words: np.ndarray) -> np.ndarray:
+        """The fused all-gather of one rank: publish its words, then collect
+        every slot. Returns uint32 words rank-major, [ranks, words]."""
+        w = np.asarray(words, dtype=np.uint32).reshape(-1)
+        self.publish_words(rank, w)
+        out = self.collect(w.size * 4)
+        return halves_to_words(out.reshape(-1)).reshape(self.ranks, w.size)
+
     # -- collect -----------------------------------------------------------
     def collect(self, nbytes: int) -> np.ndarray:
         """Collect ``nbytes`` from every rank slot of the current generation.
@@ -141,6 +169,12 @@ class MailboxModel:
     def idle(self) -> bool:
         """Every word of every generation is the sentinel."""
         return bool(np.all(self.slots == SENTINEL_U32))
+
+
+def sanitize_words(words: np.ndarray) -> np.ndarray:
+    """uint32 words with every word equal to the sentinel replaced by 0."""
+    w = np.asarray(words, dtype=np.uint32)
+    return np.where(w == SENTINEL_U32, np.uint32(0), w).astype(np.uint32)
 
 
 def allreduce_bf16(halves: np.ndarray) -> np.ndarray:
