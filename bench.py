@@ -23,6 +23,15 @@ on the host (cpu_baseline).
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--dist outliers]
     python bench.py --all-configs      # one line per configuration instead
+    python bench.py --collectives      # the mailbox consumers, one line each
+
+--collectives times the consumers of the mailbox on the m=8 N=7168 output
+(114688 bytes per rank): the fused all-gather (peers publish words, then
+mailbox_all_gather), the same unfused (every slot published, then
+mailbox_collect) and the all-reduce collect (mailbox_collect_sum). Per line:
+the whole exchange per call from a graph of K calls, the consumer kernel's
+own time from events around each eager launch, its bytes moved, parity of
+the last output against the CPU oracle, and the oracle's time per call.
 """
 
 from __future__ import annotations
@@ -57,6 +66,8 @@ def parse() -> argparse.Namespace:
                          "(the known-size reference for HBM byte counters)")
     ap.add_argument("--all-configs", action="store_true",
                     help="time every configuration (GPU and oracle), one JSON line each")
+    ap.add_argument("--collectives", action="store_true",
+                    help="time the mailbox consumers (all-gather, all-reduce), one line each")
     return ap.parse_args()
 
 
@@ -429,6 +440,134 @@ def all_configs(args) -> int:
     return 0
 
 
+def collectives(args) -> int:
+    """The mailbox consumers at the m=8 N=7168 output size, R rank slots."""
+    import numpy as np
+    import torch
+
+    from mxfp8_decode_gemm_amd import binding as mx
+    from mxfp8_decode_gemm_amd import device as dv
+    from workloads import generate
+
+    nbytes = 2 * 8 * 7168
+    words = nbytes // 4
+    K = args.steps
+    cores, model = host_cpu()
+    cases = [("all_gather_fused", r) for r in (2, 4, 8)]
+    cases += [("all_gather_unfused", r) for r in (2, 4, 8)]
+    cases += [("all_reduce", r) for r in (2, 4, 8)]
+    for op, ranks in cases:
+        seed = 7000 + ranks
+        if op == "all_reduce":
+            halves = generate.peer_payloads(seed, ranks + 1, 8, 7168)  # [ranks, 8, 7168]
+            pay_dev = [dv.upload(halves[r]) for r in range(ranks)]
+            out = torch.empty(words * 2, dtype=torch.int16, device="cuda")
+        else:
+            pay = generate.word_payloads(seed, ranks, words)
+            pay_dev = [torch.from_numpy(pay[r].view(np.int32).copy()).cuda()
+                       for r in range(ranks)]
+            out = torch.empty(ranks * words, dtype=torch.int32, device="cuda")
+        mbx = dv.Mailbox(ranks, nbytes)
+        s = torch.cuda.Stream()
+
+        def publishes():
+            if op == "all_reduce":
+                for r in range(ranks):
+                    mx.mailbox_publish(mbx.mb, r, pay_dev[r], nbytes, s)
+            else:
+                for r in range(0 if op == "all_gather_unfused" else 1, ranks):
+                    mx.mailbox_publish_words(mbx.mb, r, pay_dev[r], nbytes, s)
+
+        def consume():
+            if op == "all_gather_fused":
+                mx.mailbox_all_gather(mbx.mb, pay_dev[0], out, nbytes, s)
+            elif op == "all_gather_unfused":
+                mx.mailbox_collect(mbx.mb, out, nbytes, s)
+            else:
+                mx.mailbox_collect_sum(mbx.mb, out, nbytes, s)
+
+        calls = 0
+        with torch.cuda.stream(s):
+            for _ in range(args.warmup):
+                publishes()
+                consume()
+                calls += 1
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(K)]
+            for a, b in ev:
+                publishes()
+                a.record(s)
+                consume()
+                b.record(s)
+                calls += 1
+            torch.cuda.synchronize()
+            op_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+            mx.mxg_graph_begin(s)
+            for _ in range(K):
+                publishes()
+                consume()
+            g = mx.mxg_graph_end(s)
+            call_us = 0.0
+            for _ in range(2):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                mx.mxg_graph_launch(g, s)
+                e1.record(s)
+                torch.cuda.synchronize()
+                call_us = e0.elapsed_time(e1) * 1e3 / K
+                calls += K
+            mx.mxg_graph_destroy(g)
+        st = mbx.state_words()
+        state_ok = bool(st[mx.STATE_NEXT] == calls % 3 and st[mx.STATE_ERROR] == 0)
+        # bytes the consumer kernel moves: reads of every polled slot (and
+        # the caller's own input when fused), writes of the output and of the
+        # sentinel back into every polled slot
+        polled = ranks - 1 if op == "all_gather_fused" else ranks
+        if op == "all_reduce":
+            op_bytes = polled * nbytes + nbytes + polled * nbytes
+        else:
+            op_bytes = (polled * nbytes + (nbytes if op == "all_gather_fused" else 0)
+                        + ranks * nbytes + polled * nbytes)
+        mean_us = float(np.mean(op_us))
+        line = {"mode": "collectives", "op": op, "ranks": ranks, "nbytes_per_rank": nbytes,
+                "seed": seed, "call_us": round(call_us, 3),
+                "op_event_us": {"mean": round(mean_us, 3), "min": round(min(op_us), 3)},
+                "op_bytes": op_bytes,
+                "op_gbs": round(op_bytes / (mean_us * 1e-6) / 1e9, 1),
+                "op_frac_hbm": round(op_bytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "state_ok": state_ok}
+        if not args.no_cpu_baseline:
+            from oracle import mailbox
+
+            times = []
+            for _ in range(20):
+                t0 = time.perf_counter()
+                mb = mailbox.MailboxModel(ranks, nbytes)
+                if op == "all_reduce":
+                    for r in range(ranks):
+                        mb.publish(r, halves[r])
+                    want = mb.collect_sum(nbytes).view(np.int16)
+                elif op == "all_gather_fused":
+                    for r in range(1, ranks):
+                        mb.publish_words(r, pay[r])
+                    want = mb.all_gather(0, pay[0]).reshape(-1).view(np.int32)
+                else:
+                    for r in range(ranks):
+                        mb.publish_words(r, pay[r])
+                    want = mb.collect(nbytes).reshape(-1).view(np.int32)
+                times.append(time.perf_counter() - t0)
+            sec = float(np.median(times))
+            line["cpu_baseline"] = {
+                "value": round(sec * 1e6, 1), "unit": "µs/call", "cores": 1,
+                "cpu_model": model, "kind": "oracle",
+                "sample": f"20 calls of the oracle's mailbox model ({op}, {ranks} slots of "
+                          f"{nbytes} B, numpy on one thread); median"}
+            line["parity_bit_exact"] = bool(np.array_equal(out.cpu().numpy().reshape(-1), want))
+        print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -442,6 +581,8 @@ def main() -> int:
         print("bench.py needs a HIP device", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.collectives:
+        return collectives(args)
     return all_configs(args) if args.all_configs else headline(args)
 
 

@@ -50,16 +50,27 @@ extern "C" {
 #define MXG_SCALE_BLOCK 32    /* one E8M0 scale per 32 K (sf_vec_size=32) */
 
 /* Mailbox state words (uint32). NEXT and ACTIVE are the stage words of the
- * publishing_gemm page's module docstring: [0] the generation the next
- * publish writes (advanced by the collect that empties it), [1] the
- * generation the last publish wrote. COLLECT_ARR counts collect workgroups
- * (all_gather page, step 3: the last to arrive advances the generation).
- * ERROR is a sticky bit set: MXG_ERR_* below. */
-#define MXG_STATE_WORDS 8
+ * publishing_gemm page's module docstring: [0] the generation the owner's
+ * next publish writes and its next collect reads (advanced by the collect
+ * that empties it), [1] the generation the owner's last publish wrote.
+ * COLLECT_ARR counts collect workgroups (all_gather page, step 3: the last to
+ * arrive advances the generation). ERROR is a sticky bit set: MXG_ERR_* below.
+ *
+ * PEER_GEN + r is the generation counter of emulated peer slot r (r other
+ * than the owner's rank): every rank keeps its own counter and advances it
+ * once per call (all_gather page, module docstring, step 3), so a peer never
+ * reads the owner's NEXT, which the owner's collect advances while peers may
+ * still be about to publish. A peer publish writes generation PEER_GEN[r] and
+ * the last of its workgroups to arrive (PEER_ARR + r counts them) advances
+ * PEER_GEN[r] mod 3. With one publish per peer per collect, PEER_GEN[r]
+ * equals NEXT whenever no call is in flight. */
+#define MXG_STATE_WORDS 32
 #define MXG_STATE_NEXT 0
 #define MXG_STATE_ACTIVE 1
 #define MXG_STATE_COLLECT_ARR 2
 #define MXG_STATE_ERROR 3
+#define MXG_STATE_PEER_GEN 8
+#define MXG_STATE_PEER_ARR 16
 
 /* Split-K workspace layout:
  *   [0, 256)             header, uint32 words: EPOCH, (reserved), ERROR
@@ -189,14 +200,43 @@ int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t*
                          uint16_t* c_out, void* stream, void* ev_start, void* ev_stop);
 
 /* Unfused publish: copy `nbytes` of BF16 from `src` (device, 16-B aligned)
- * into slot `rank` of generation state[NEXT] with negative zero cleared, and
- * set state[ACTIVE]. Serves as the emulated peers' publish and as the
+ * into slot `rank` with negative zero cleared. For the owner's slot
+ * (rank == mb->rank) the generation is state[NEXT] and state[ACTIVE] is set;
+ * for an emulated peer slot it is state[PEER_GEN + rank], which the call
+ * advances (see the state words above), so peers may publish on another
+ * stream while the owner's collect polls. Serves as the emulated peers' publish and as the
  * unfused path the fused epilogue must match bit for bit (publishing_gemm
  * page, module docstring: the consumer sees the same bits either way).
  * Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY (nbytes outside
  * (0, capacity] or not a multiple of 16), MXG_EHIP. */
 int mailbox_publish(const mxg_mailbox* mb, int32_t rank, const void* src,
                     int64_t nbytes, void* stream);
+
+/* Word publish: mailbox_publish for payloads of arbitrary 32-bit words (the
+ * all-gather's input; all_gather page, module docstring, step 1): each word
+ * equal to the sentinel 0x80000000 is written as 0, every other word as it
+ * is. Serves as the emulated peers' publish for mailbox_all_gather and as its
+ * unfused counterpart. Arguments and errors as mailbox_publish. */
+int mailbox_publish_words(const mxg_mailbox* mb, int32_t rank, const void* src,
+                          int64_t nbytes, void* stream);
+
+/* Fused all-gather of one rank (all_gather page, module docstring, steps
+ * 1-3; _AllGatherKernel.kernel), the caller being slot mb->rank: one kernel
+ * writes the caller's payload `src` (nbytes, words equal to the sentinel
+ * sent as 0) to out + rank * nbytes and, for every other rank r and pack
+ * p < nbytes/16 of generation g = state[NEXT], polls the pack until none of
+ * its words is the sentinel, writes it to out + (r * nbytes + 16 p), and
+ * stores the sentinel back; the last workgroup sets state[NEXT] = (g+1) mod 3.
+ * Equivalent to mailbox_publish_words(mb, mb->rank, src) followed by
+ * mailbox_collect, except that the caller's own slot is never written (the
+ * same thread would store, reload and reset it: same end state). Peers
+ * publish with mailbox_publish_words before or during the call. `src` and
+ * `out` are device memory, 16-B aligned; `out` holds ranks * nbytes bytes;
+ * `src` may be exactly out + rank * nbytes (in place) and must not overlap
+ * `out` otherwise. Spin limit and MXG_ERR_COLLECT_SPIN as mailbox_collect.
+ * Errors: MXG_EINVAL (null, overlap), MXG_EALIGN, MXG_ECAPACITY, MXG_EHIP. */
+int mailbox_all_gather(const mxg_mailbox* mb, const void* src, void* out, int64_t nbytes,
+                       void* stream);
 
 /* Collect (all_gather page, module docstring, step 2; _AllGatherKernel.kernel):
  * for every rank r and pack p < nbytes/16 of generation g = state[NEXT],

@@ -30,8 +30,9 @@ PACK_BYTES = 16
 SENTINEL = 0x80000000
 MAX_RANKS = 8
 MAX_ROWS = 8
-STATE_WORDS = 8
+STATE_WORDS = 32
 STATE_NEXT, STATE_ACTIVE, STATE_COLLECT_ARR, STATE_ERROR = 0, 1, 2, 3
+STATE_PEER_GEN, STATE_PEER_ARR = 8, 16
 WS_HEADER_BYTES = 256
 WS_FLAG_BYTES = 8192
 WS_MAX_GROUPS = 2048
@@ -95,6 +96,8 @@ def _load() -> ctypes.CDLL:
         "mailbox_publish": (ctypes.c_int, [mbp, i32, vp, i64, vp]),
         "mailbox_collect": (ctypes.c_int, [mbp, vp, i64, vp]),
         "mailbox_collect_sum": (ctypes.c_int, [mbp, vp, i64, vp]),
+        "mailbox_publish_words": (ctypes.c_int, [mbp, i32, vp, i64, vp]),
+        "mailbox_all_gather": (ctypes.c_int, [mbp, vp, vp, i64, vp]),
         "mxg_set_spin_limit": (u32, [u32]),
         "mxg_graph_begin": (ctypes.c_int, [vp]),
         "mxg_graph_end": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
@@ -245,6 +248,16 @@ def mailbox_collect(mb: mxg_mailbox, out, nbytes: int, stream=None) -> None:
 def mailbox_collect_sum(mb: mxg_mailbox, out, nbytes: int, stream=None) -> None:
     _check(_lib.mailbox_collect_sum(ctypes.byref(mb), _ptr(out), nbytes, _stream(stream)),
            "mailbox_collect_sum")
+
+
+def mailbox_publish_words(mb: mxg_mailbox, rank: int, src, nbytes: int, stream=None) -> None:
+    _check(_lib.mailbox_publish_words(ctypes.byref(mb), rank, _ptr(src), nbytes,
+                                      _stream(stream)), "mailbox_publish_words")
+
+
+def mailbox_all_gather(mb: mxg_mailbox, src, out, nbytes: int, stream=None) -> None:
+    _check(_lib.mailbox_all_gather(ctypes.byref(mb), _ptr(src), _ptr(out), nbytes,
+                                   _stream(stream)), "mailbox_all_gather")
 
 
 def mxg_set_spin_limit(polls: int) -> int:

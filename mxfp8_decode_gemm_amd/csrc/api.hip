@@ -167,16 +167,47 @@ int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t*
                       c_out, stream, ev_start, ev_stop);
 }
 
-int mailbox_publish(const mxg_mailbox* mb, int32_t rank, const void* src, int64_t nbytes,
-                    void* stream) {
+namespace {
+int slot_publish_impl(const mxg_mailbox* mb, int32_t rank, const void* src, int64_t nbytes,
+                      bool words, void* stream) {
   if (!mailbox_ok(mb) || !src || rank < 0 || rank >= mb->ranks) return MXG_EINVAL;
   if (!aligned16(src) || !aligned16(mb->slots) || !aligned16(mb->state)) return MXG_EALIGN;
   if (nbytes <= 0 || nbytes > mb->capacity_bytes || nbytes % MXG_PACK_BYTES)
     return MXG_ECAPACITY;
   uint8_t* slot = static_cast<uint8_t*>(mb->slots) + (size_t)rank * mb->capacity_bytes;
   return hip_code(launch_mailbox_publish(slot, (int64_t)mb->ranks * mb->capacity_bytes,
-                                         mb->state, static_cast<const uint8_t*>(src), nbytes,
-                                         static_cast<hipStream_t>(stream)));
+                                         mb->state, rank == mb->rank ? -1 : rank,
+                                         static_cast<const uint8_t*>(src), nbytes,
+                                         words, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int mailbox_publish(const mxg_mailbox* mb, int32_t rank, const void* src, int64_t nbytes,
+                    void* stream) {
+  return slot_publish_impl(mb, rank, src, nbytes, false, stream);
+}
+
+int mailbox_publish_words(const mxg_mailbox* mb, int32_t rank, const void* src, int64_t nbytes,
+                          void* stream) {
+  return slot_publish_impl(mb, rank, src, nbytes, true, stream);
+}
+
+int mailbox_all_gather(const mxg_mailbox* mb, const void* src, void* out, int64_t nbytes,
+                       void* stream) {
+  if (!mailbox_ok(mb) || !src || !out) return MXG_EINVAL;
+  if (!aligned16(src) || !aligned16(out) || !aligned16(mb->slots) || !aligned16(mb->state))
+    return MXG_EALIGN;
+  if (nbytes <= 0 || nbytes > mb->capacity_bytes || nbytes % MXG_PACK_BYTES)
+    return MXG_ECAPACITY;
+  // src must not overlap out, except as exactly the caller's own output row.
+  const uint8_t* s = static_cast<const uint8_t*>(src);
+  const uint8_t* o = static_cast<const uint8_t*>(out);
+  const uint8_t* own = o + (size_t)mb->rank * nbytes;
+  if (s != own && s < o + (size_t)mb->ranks * nbytes && o < s + nbytes) return MXG_EINVAL;
+  return hip_code(launch_mailbox_all_gather(
+      static_cast<uint8_t*>(mb->slots), (int64_t)mb->ranks * mb->capacity_bytes,
+      mb->capacity_bytes, mb->ranks, mb->rank, mb->state, s, static_cast<uint8_t*>(out),
+      nbytes, spin_limit(), static_cast<hipStream_t>(stream)));
 }
 
 int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream) {

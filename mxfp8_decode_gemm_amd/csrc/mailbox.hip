@@ -13,8 +13,10 @@
 //     its words is the sentinel, copies it out rank-major, stores the
 //     sentinel back, and the last workgroup to arrive advances the
 //     generation mod 3.
-// All payload traffic moves as 32-bit integers, never through float
-// registers (sync page, Mailbox.put_words: a NaN bit pattern would not
+// The all-gather variant (same module docstring, step 1) moves arbitrary
+// 32-bit words: a word equal to the sentinel goes out as 0, every other word
+// unchanged. All payload traffic moves as 32-bit integers, never through
+// float registers (sync page, Mailbox.put_words: a NaN bit pattern would not
 // survive a float move).
 
 #include <hip/hip_runtime.h>
@@ -44,6 +46,25 @@ __device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
   return lo | hi;
 }
 
+__device__ __forceinline__ uint32_t clear_sentinel_word(uint32_t w) {
+  return w == MXG_SENTINEL ? 0u : w;
+}
+
+__device__ __forceinline__ uint4 sanitize_pack(uint4 v, bool words) {
+  if (words) {
+    v.x = clear_sentinel_word(v.x);
+    v.y = clear_sentinel_word(v.y);
+    v.z = clear_sentinel_word(v.z);
+    v.w = clear_sentinel_word(v.w);
+  } else {
+    v.x = clear_negative_zero(v.x);
+    v.y = clear_negative_zero(v.y);
+    v.z = clear_negative_zero(v.z);
+    v.w = clear_negative_zero(v.w);
+  }
+  return v;
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t words, uint32_t value) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   const size_t quads = words / 4;
@@ -64,22 +85,34 @@ __global__ void workspace_header_kernel(uint32_t* hdr) {
   if (i < MXG_WS_HEADER_BYTES / 4) hdr[i] = i == MXG_WS_EPOCH ? 1u : 0u;
 }
 
-// Unfused publish: one thread per 16-byte pack.
-__global__ void publish_kernel(uint8_t* slot, int64_t gen_stride, uint32_t* state,
+// Unfused publish: one thread per 16-byte pack. kWords selects the word
+// rule (sentinel words become 0) over the BF16 rule (negative zero cleared).
+// peer < 0 publishes the owner's slot in generation NEXT and sets ACTIVE; a
+// peer slot publishes in its own generation PEER_GEN[peer], which the last
+// workgroup to arrive advances at its end (the same hand-off as the collect:
+// every workgroup counts itself only after its generation load returned).
+template <bool kWords>
+__global__ void publish_kernel(uint8_t* slot, int64_t gen_stride, uint32_t* state, int peer,
                                const uint8_t* src, int64_t packs) {
-  const uint32_t gen = ld_agent_u32(state + MXG_STATE_NEXT) % MXG_GENERATIONS;
+  uint32_t* gen_word = peer < 0 ? state + MXG_STATE_NEXT : state + MXG_STATE_PEER_GEN + peer;
+  const uint32_t graw = ld_agent_u32(gen_word);
+  const uint32_t gen = graw % MXG_GENERATIONS;
+  uint32_t arrived = 0;
+  if (peer >= 0 && threadIdx.x == 0)
+    arrived = __hip_atomic_fetch_add(state + MXG_STATE_PEER_ARR + peer,
+                                     1u + (graw == 0xFFFFFFFFu ? 1u : 0u), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
   uint4* dst = reinterpret_cast<uint4*>(slot + (size_t)gen * gen_stride);
   const uint4* s = reinterpret_cast<const uint4*>(src);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < packs; p += stride) {
-    uint4 v = s[p];
-    v.x = clear_negative_zero(v.x);
-    v.y = clear_negative_zero(v.y);
-    v.z = clear_negative_zero(v.z);
-    v.w = clear_negative_zero(v.w);
-    dst[p] = v;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < packs; p += stride)
+    dst[p] = sanitize_pack(s[p], kWords);
+  if (peer < 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) st_agent_u32(state + MXG_STATE_ACTIVE, gen);
+  } else if (threadIdx.x == 0 && arrived == gridDim.x - 1u) {
+    st_agent_u32(state + MXG_STATE_PEER_ARR + peer, 0u);
+    st_agent_u32(gen_word, (gen + 1u) % MXG_GENERATIONS);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) st_agent_u32(state + MXG_STATE_ACTIVE, gen);
 }
 
 // Collect: one thread per (rank, pack), grid-stride. Every thread loads the
@@ -90,16 +123,23 @@ __global__ void publish_kernel(uint8_t* slot, int64_t gen_stride, uint32_t* stat
 // arrive advances the generation at its end (all_gather page, step 3). No
 // workgroup of this launch can read the advanced value: every read returned
 // before its workgroup's count, and the advancing store follows the last one.
+//
+// kGather fuses the caller's own publish (all_gather page, _AllGatherKernel):
+// the items of rank `self` come from `src` with sentinel words sent as 0,
+// straight to the output. The own slot is left untouched: publishing into it
+// and polling it back would be the same thread storing, reloading and
+// resetting its own pack, which ends in the same state.
+template <bool kGather>
 __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capacity, int ranks,
                                uint32_t* state, uint8_t* out, int64_t nbytes,
-                               uint32_t spin_limit) {
+                               uint32_t spin_limit, const uint8_t* src, int self) {
   const int64_t packs = nbytes / MXG_PACK_BYTES;
   const int64_t total = packs * ranks;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const uint32_t graw = ld_agent_u32(state + MXG_STATE_NEXT);
   uint64_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0, lo2 = 0, hi2 = 0;
-  if (i0 < total) {
+  if (i0 < total && !(kGather && i0 / packs == self)) {
     const int64_t r = i0 / packs;
     const uint64_t* s0 = reinterpret_cast<const uint64_t*>(
         slots + r * capacity + (i0 - r * packs) * MXG_PACK_BYTES);
@@ -122,6 +162,11 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
   for (int64_t i = i0; i < total; i += stride) {
     const int64_t r = i / packs;
     const int64_t p = i - r * packs;
+    if (kGather && r == self) {
+      *reinterpret_cast<uint4*>(out + r * nbytes + p * MXG_PACK_BYTES) =
+          sanitize_pack(*reinterpret_cast<const uint4*>(src + p * MXG_PACK_BYTES), true);
+      continue;
+    }
     uint64_t* slot = reinterpret_cast<uint64_t*>(base + r * capacity + p * MXG_PACK_BYTES);
     uint64_t lo, hi;
     if (i == i0) {
@@ -272,10 +317,15 @@ hipError_t launch_workspace_init(uint32_t* ws, size_t bytes, hipStream_t s) {
 }
 
 hipError_t launch_mailbox_publish(uint8_t* slot, int64_t gen_stride, uint32_t* state,
-                                  const uint8_t* src, int64_t nbytes, hipStream_t s) {
+                                  int peer, const uint8_t* src, int64_t nbytes, bool words,
+                                  hipStream_t s) {
   const int64_t packs = nbytes / MXG_PACK_BYTES;
-  hipLaunchKernelGGL(publish_kernel, dim3(blocks_for(packs)), dim3(kThreads), 0, s, slot,
-                     gen_stride, state, src, packs);
+  if (words)
+    hipLaunchKernelGGL(publish_kernel<true>, dim3(blocks_for(packs)), dim3(kThreads), 0, s,
+                       slot, gen_stride, state, peer, src, packs);
+  else
+    hipLaunchKernelGGL(publish_kernel<false>, dim3(blocks_for(packs)), dim3(kThreads), 0, s,
+                       slot, gen_stride, state, peer, src, packs);
   return hipGetLastError();
 }
 
@@ -283,8 +333,20 @@ hipError_t launch_mailbox_collect(uint8_t* slots, int64_t gen_stride, int64_t ca
                                   int ranks, uint32_t* state, uint8_t* out, int64_t nbytes,
                                   uint32_t spin_limit, hipStream_t s) {
   const int64_t items = nbytes / MXG_PACK_BYTES * ranks;
-  hipLaunchKernelGGL(collect_kernel, dim3(blocks_for(items)), dim3(kThreads), 0, s, slots,
-                     gen_stride, capacity, ranks, state, out, nbytes, spin_limit);
+  hipLaunchKernelGGL(collect_kernel<false>, dim3(blocks_for(items)), dim3(kThreads), 0, s,
+                     slots, gen_stride, capacity, ranks, state, out, nbytes, spin_limit,
+                     (const uint8_t*)nullptr, -1);
+  return hipGetLastError();
+}
+
+hipError_t launch_mailbox_all_gather(uint8_t* slots, int64_t gen_stride, int64_t capacity,
+                                     int ranks, int self, uint32_t* state, const uint8_t* src,
+                                     uint8_t* out, int64_t nbytes, uint32_t spin_limit,
+                                     hipStream_t s) {
+  const int64_t items = nbytes / MXG_PACK_BYTES * ranks;
+  hipLaunchKernelGGL(collect_kernel<true>, dim3(blocks_for(items)), dim3(kThreads), 0, s,
+                     slots, gen_stride, capacity, ranks, state, out, nbytes, spin_limit, src,
+                     self);
   return hipGetLastError();
 }
 

@@ -67,13 +67,19 @@ hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_
 hipError_t launch_state_init(uint32_t* state, hipStream_t s);
 hipError_t launch_workspace_init(uint32_t* ws, size_t bytes, hipStream_t s);
 hipError_t launch_mailbox_publish(uint8_t* slot, int64_t gen_stride, uint32_t* state,
-                                  const uint8_t* src, int64_t nbytes, hipStream_t s);
+                                  int peer, const uint8_t* src, int64_t nbytes, bool words,
+                                  hipStream_t s);
 hipError_t launch_mailbox_collect(uint8_t* slots, int64_t gen_stride, int64_t capacity,
                                   int ranks, uint32_t* state, uint8_t* out,
                                   int64_t nbytes, uint32_t spin_limit, hipStream_t s);
 hipError_t launch_mailbox_collect_sum(uint8_t* slots, int64_t gen_stride, int64_t capacity,
                                       int ranks, uint32_t* state, uint8_t* out, int64_t nbytes,
                                       uint32_t spin_limit, hipStream_t s);
+
+hipError_t launch_mailbox_all_gather(uint8_t* slots, int64_t gen_stride, int64_t capacity,
+                                     int ranks, int self, uint32_t* state, const uint8_t* src,
+                                     uint8_t* out, int64_t nbytes, uint32_t spin_limit,
+                                     hipStream_t s);
 
 uint32_t spin_limit();
 

@@ -113,6 +113,17 @@ def collect_sum(mailbox: Mailbox, nbytes: int, out: torch.Tensor = None,
     return out
 
 
+def all_gather(mailbox: Mailbox, src: torch.Tensor, nbytes: int, out: torch.Tensor = None,
+               stream=None) -> torch.Tensor:
+    """One mailbox_all_gather of slot mailbox.rank; returns the [ranks * nbytes]
+    byte output as int32 words."""
+    if out is None:
+        out = torch.empty(mailbox.ranks * nbytes // 4, dtype=torch.int32,
+                          device=mailbox.slots.device)
+    mx.mailbox_all_gather(mailbox.mb, src, out, nbytes, stream)
+    return out
+
+
 def as_u16(t: torch.Tensor) -> np.ndarray:
     """uint16 host copy of a 16-bit device tensor."""
     return t.cpu().numpy().view(np.uint16).copy()

@@ -88,7 +88,12 @@ def words_to_halves(words: np.ndarray) -> np.ndarray:
 
 
 class MailboxModel:
-    """Host model of one mailbox with ``ranks`` emulated rank slots."""
+    """Host model of one mailbox with ``ranks`` emulated rank slots.
+
+    One generation counter serves every slot. Each rank keeps its own counter
+    and advances it once per call (all_gather page, module docstring, step
+    3); when every peer publishes once per collect, all the counters agree
+    with this one between calls."""
 
     def __init__(self, ranks: int, capacity_bytes: int) -> None:
         if not 1 <= ranks <= MAX_RANKS:

@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -32,7 +32,10 @@ def test_header_constants_match_binding(mx):
     with open(os.path.join(ROOT, "include", "mxgemm.h")) as f:
         h = f.read()
     for name, val in [("MXG_GENERATIONS", 3), ("MXG_PACK_BYTES", 16), ("MXG_MAX_ROWS", 8),
-                      ("MXG_STATE_NEXT", 0), ("MXG_STATE_ACTIVE", 1), ("MXG_WS_EPOCH", 0)]:
+                      ("MXG_STATE_NEXT", 0), ("MXG_STATE_ACTIVE", 1), ("MXG_WS_EPOCH", 0),
+                      ("MXG_STATE_WORDS", mx.STATE_WORDS),
+                      ("MXG_STATE_PEER_GEN", mx.STATE_PEER_GEN),
+                      ("MXG_STATE_PEER_ARR", mx.STATE_PEER_ARR)]:
         assert f"#define {name} {val}" in h
     assert "#define MXG_SENTINEL 0x80000000u" in h
     assert mx.SENTINEL == 0x80000000 and mx.GENERATIONS == 3
@@ -101,6 +104,21 @@ def test_collect_and_publish_capacity(mx, nbytes, code):
     assert lib.mailbox_collect(ctypes.byref(mb), 4100, 16, None) == -2
     assert lib.mailbox_collect_sum(ctypes.byref(mb), 4100, 16, None) == -2
     assert lib.mailbox_collect_sum(ctypes.byref(mb), None, 16, None) == -1
+    assert lib.mailbox_publish_words(ctypes.byref(mb), 0, 4096, nbytes, None) == code
+    assert lib.mailbox_publish_words(ctypes.byref(mb), 1, 4096, 16, None) == -1
+    assert lib.mailbox_all_gather(ctypes.byref(mb), 8192, 4096, nbytes, None) == code
+    assert lib.mailbox_all_gather(ctypes.byref(mb), 8200, 4096, 16, None) == -2
+    assert lib.mailbox_all_gather(ctypes.byref(mb), None, 4096, 16, None) == -1
+
+
+def test_all_gather_overlap(mx):
+    """src may be exactly the caller's own output row, nothing else in out."""
+    lib = mx.library()
+    mb = _mb(mx, ranks=2, rank=1)
+    # out = [4096, 4096 + 2*64); own row at 4096 + 64
+    assert lib.mailbox_all_gather(ctypes.byref(mb), 4096, 4096, 64, None) == -1
+    assert lib.mailbox_all_gather(ctypes.byref(mb), 4096 + 48, 4096, 64, None) == -1
+    assert lib.mailbox_all_gather(ctypes.byref(mb), 4096 - 48, 4096, 64, None) == -1
 
 
 def test_pack_sizes_and_validation(mx):

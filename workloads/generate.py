@@ -16,6 +16,8 @@ optional split-K). These generators stand in for it with seeded Gaussian data:
 * Peer payloads for emulated rank slots are BF16 bit patterns of Gaussians
   with about 1 % of halves forced to 0x8000 and some 32-bit words forced to
   0x80000000 (the Lamport sentinel), which the publish must turn into 0.
+* All-gather payloads are uniform random 32-bit words with about 1 % set to
+  the sentinel and 1 % to its near neighbours.
 
 Seeds: 20261202 + 100 * config_index + variant, with variant = m + 16 * split_k
 for the N=4096 sweep and 0 otherwise.
@@ -214,3 +216,19 @@ def peer_payloads(seed: int, ranks: int, m: int, n: int) -> np.ndarray:
         words[sent, 0] = 0x0000
         words[sent, 1] = 0x8000
     return bits
+
+
+def word_payloads(seed: int, ranks: int, words: int) -> np.ndarray:
+    """uint32 payloads [ranks, words] for an all-gather of arbitrary words:
+    uniform random bits with about 1 % of the words set to the sentinel
+    0x80000000 and about 1 % to neighbours of it (0x80000001, 0x7FFFFFFF,
+    0x00008000, 0x80008000), so that the word rule meets both."""
+    rng = np.random.default_rng(seed ^ 0xA11C)
+    out = rng.integers(0, 2**32, size=(ranks, words), dtype=np.uint64).astype(np.uint32)
+    flat = out.reshape(-1)
+    hits = max(1, flat.size // 100)
+    flat[rng.choice(flat.size, size=hits, replace=False)] = 0x80000000
+    near = np.array([0x80000001, 0x7FFFFFFF, 0x00008000, 0x80008000], dtype=np.uint32)
+    idx = rng.choice(flat.size, size=hits, replace=False)
+    flat[idx] = near[rng.integers(0, near.size, size=hits)]
+    return out
