@@ -19,6 +19,14 @@ one E8M0 scale per 32 consecutive elements along K:
 
 This module loops in pure Python and is meant for small arrays; it pins the
 vectorized input generator bit for bit.
+
+``quantize_bf16`` is the activation quantizer in front of the GEMM
+(publishing_gemm page, ``PublishingMxfp8Linear.__call__``: the activation is
+an MXFP8 QuantizedActivation whose original dtype is BF16). The pages do not
+print the quantizer; it applies the rule above to the BF16 values, which are
+exact in float64. Reading for what the rule leaves open: a block whose largest
+magnitude is infinite or NaN gets scale byte 0xFF (the E8M0 NaN) and every
+code of the block is the e4m3fn NaN 0x7F with the element's sign bit.
 """
 
 from __future__ import annotations
@@ -89,4 +97,39 @@ def quantize_mxfp8(values: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
             scales[r, b] = e + 127
             for j, v in enumerate(block):
                 codes[r, b * BLOCK + j] = e4m3_round(math.ldexp(v, -e))
+    return codes, scales
+
+
+E8M0_NAN = 0xFF
+E4M3_NAN = 0x7F
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """float64 values of uint16 BF16 bit patterns (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def quantize_bf16(bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize a [rows, K] array of BF16 bit patterns (uint16) to e4m3fn codes
+    [rows, K] and E8M0 scale bytes [rows, K/32]: finite blocks as
+    quantize_mxfp8, non-finite blocks as the reading in the module docstring."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    rows, k = bits.shape
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    vals = bf16_bits_to_f64(bits)
+    codes = np.zeros((rows, k), dtype=np.uint8)
+    scales = np.zeros((rows, k // BLOCK), dtype=np.uint8)
+    for r in range(rows):
+        for b in range(k // BLOCK):
+            sl = slice(b * BLOCK, (b + 1) * BLOCK)
+            if np.all(np.isfinite(vals[r, sl])):
+                c, sc = quantize_mxfp8(vals[r:r + 1, sl])
+                codes[r, sl] = c[0]
+                scales[r, b] = sc[0, 0]
+            else:
+                sign = (bits[r, sl] >> np.uint16(8)).astype(np.uint8) & np.uint8(0x80)
+                codes[r, sl] = sign | np.uint8(E4M3_NAN)
+                scales[r, b] = E8M0_NAN
     return codes, scales
