@@ -24,6 +24,7 @@ on the host (cpu_baseline).
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--dist outliers]
     python bench.py --all-configs      # one line per configuration instead
     python bench.py --collectives      # the mailbox consumers, one line each
+    python bench.py --activation-quant # BF16 activations: fused vs unfused lines
 
 --collectives times the consumers of the mailbox on the m=8 N=7168 output
 (114688 bytes per rank): the fused all-gather (peers publish words, then
@@ -32,6 +33,14 @@ mailbox_collect) and the all-reduce collect (mailbox_collect_sum). Per line:
 the whole exchange per call from a graph of K calls, the consumer kernel's
 own time from events around each eager launch, its bytes moved, parity of
 the last output against the CPU oracle, and the oracle's time per call.
+
+--activation-quant times the headline workload with a BF16 activation
+(N(0,1), 1 % of channels x50, rounded to BF16): quantized inside the GEMM
+(mxgemm_publish_bf16) against quantized by its own kernel first
+(mxfp8_quantize, then mxgemm_publish), and the publish fused into the GEMM
+against the page's unfused path (mxgemm writes C, mailbox_publish reads it
+back). Each variant: a graph of K whole steps (with the collect) and a graph
+of K launches of its kernels alone.
 """
 
 from __future__ import annotations
@@ -68,12 +77,14 @@ def parse() -> argparse.Namespace:
                     help="time every configuration (GPU and oracle), one JSON line each")
     ap.add_argument("--collectives", action="store_true",
                     help="time the mailbox consumers (all-gather, all-reduce), one line each")
+    ap.add_argument("--activation-quant", action="store_true",
+                    help="time the BF16-activation and unfused-publish variants, one line each")
     return ap.parse_args()
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_publish_n7168_k8192_m8_s4_hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "mxfp8_decode_gemm_amd", "csrc", f)
-                  for f in ("gemm_publish.hip", "mxgemm_internal.h")]
+                  for f in ("gemm_publish.hip", "mxgemm_internal.h", "quant_device.h")]
 
 
 def kernel_source_hash() -> str:
@@ -568,6 +579,109 @@ def collectives(args) -> int:
     return 0
 
 
+def activation_quant(args) -> int:
+    """Fused and unfused variants of the headline step, one line each."""
+    import numpy as np
+    import torch
+
+    from workloads import generate
+
+    p = generate.config_problem(2)
+    xbits = generate.bf16_activation(p.seed, p.m, p.k, "outliers")
+    run = Runner(p, p.split_k, 1, p.out_bytes, args.cold_mib)
+    mx, dv, s = run.mx, run.dv, run.stream
+    xb = dv.upload(xbits)
+    xq = torch.empty(p.m * p.k, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(p.m * p.k // 32, dtype=torch.uint8, device="cuda")
+    c = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
+    wsb, wsn = run.wsp.buf, run.wsp.nbytes
+    K = args.steps
+
+    def w(i):
+        return run.w[i % run.copies]
+
+    def fused_quant(i):
+        wi, wsi = w(i)
+        mx.mxgemm_publish_bf16(run.mbx.mb, wi, wsi, xb, p.m, p.n, p.k, p.split_k, wsb, wsn,
+                               None, None, None, s)
+        run.gemm_calls += 1
+
+    def unfused_quant(i):
+        mx.mxfp8_quantize(xb, p.m, p.k, xq, xs, s)
+        wi, wsi = w(i)
+        mx.mxgemm_publish(run.mbx.mb, wi, wsi, xq, xs, p.m, p.n, p.k, p.split_k, wsb, wsn, None,
+                          s)
+        run.gemm_calls += 1
+
+    def fused_publish(i):
+        run.gemm(i)
+
+    def unfused_publish(i):
+        wi, wsi = w(i)
+        mx.mxgemm(wi, wsi, run.x, run.xs, p.m, p.n, p.k, p.split_k, wsb, wsn, c, s)
+        run.gemm_calls += 1
+        mx.mailbox_publish(run.mbx.mb, 0, c, p.out_bytes, s)
+
+    variants = [("quant_fused", "mxgemm_publish_bf16", fused_quant),
+                ("quant_unfused", "mxfp8_quantize + mxgemm_publish", unfused_quant),
+                ("publish_fused", "mxgemm_publish", fused_publish),
+                ("publish_unfused", "mxgemm + mailbox_publish", unfused_publish)]
+    lines = []
+    with torch.cuda.stream(s):
+        for name, calls, body in variants:
+            for i in range(args.warmup):
+                body(i)
+                run.collect()
+            torch.cuda.synchronize()
+            # kernels alone: K back-to-back calls, the mailbox drained after
+            # each replay (every call republishes into the same generation)
+            kern_ms = run.graph_ms(lambda: [body(i) for i in range(K)], K, after=run.collect)
+            step_ms = run.graph_ms(lambda: [(body(i), run.collect()) for i in range(K)], K)
+            lines.append((name, calls, kern_ms, step_ms))
+        state_ok = run.state_ok()
+    algo = p.algorithmic_bytes()
+    extra = {"quant_fused": p.m * p.k * 2 - p.m * p.k - p.m * p.k // 32,
+             "quant_unfused": p.m * p.k * 2 - p.m * p.k - p.m * p.k // 32}
+    out = []
+    for name, calls, kern_ms, step_ms in lines:
+        b = algo + extra.get(name, 0)
+        out.append({"mode": "activation_quant", "variant": name, "calls": calls,
+                    "workload": "N=7168 K=8192 m=8 split-K 4, BF16 activation (N(0,1), 1 % of "
+                                "channels x50)" if name.startswith("quant") else
+                                "N=7168 K=8192 m=8 split-K 4, MXFP8 activation",
+                    "kernels_us": round(kern_ms * 1e3, 3), "step_us": round(step_ms * 1e3, 3),
+                    "algorithmic_bytes": b,
+                    "kernels_gbs": round(b / (kern_ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(b / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "state_ok": state_ok})
+    if not args.no_cpu_baseline:
+        from oracle import gemm, quant
+
+        cores, model = host_cpu()
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oq, osc = quant.quantize_bf16(xbits)
+            gemm.gemm_publish_bits(p.w, p.ws, oq, osc)
+            times.append(time.perf_counter() - t0)
+        sec = float(np.median(times))
+        mx.mxgemm_publish_bf16(run.mbx.mb, run.w[0][0], run.w[0][1], xb, p.m, p.n, p.k,
+                               p.split_k, wsb, wsn, None, xq, xs, s)
+        run.collect()
+        torch.cuda.synchronize()
+        exact = (np.array_equal(xq.cpu().numpy().reshape(p.m, p.k), oq)
+                 and np.array_equal(xs.cpu().numpy().reshape(p.m, p.k // 32), osc))
+        cpu = {"value": round(sec * 1e6, 1), "unit": "µs/call", "cores": cores,
+               "cpu_model": model, "kind": "oracle",
+               "sample": "3 calls of the oracle's BF16 quantizer (pure Python, one thread) and "
+                         "float64 GEMM on the same workload; median"}
+        out[0]["cpu_baseline"] = cpu
+        out[0]["quantized_activation_bit_exact"] = bool(exact)
+    for line in out:
+        print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -583,6 +697,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.collectives:
         return collectives(args)
+    if args.activation_quant:
+        return activation_quant(args)
     return all_configs(args) if args.all_configs else headline(args)
 
 

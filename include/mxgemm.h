@@ -199,6 +199,44 @@ int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t*
                          int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
                          uint16_t* c_out, void* stream, void* ev_start, void* ev_stop);
 
+/* mxgemm_publish with the activation in BF16, quantized inside the GEMM
+ * (the MXFP8 activation the publishing_gemm page's PublishingMxfp8Linear
+ * takes is a QuantizedActivation whose original dtype is BF16; the quantizer
+ * itself is not printed). Each workgroup quantizes the K slice of x it
+ * needs while its first W loads are in flight: per row and 32 consecutive K,
+ * e = the smallest integer with max|x| <= 448 * 2^e, clamped to [-127, 127]
+ * (an all-zero block: -127), scale byte e + 127, and each element the
+ * e4m3fn value nearest to x / 2^e (ties to even, sign kept). A block holding
+ * an infinity or NaN gets scale byte 0xFF and codes 0x7F | sign. The product
+ * then is mxgemm_publish's on those codes and scales.
+ *   x            device [m, k] BF16 row-major, 16-B aligned.
+ *   x_q_out, x_scale_out  both NULL, or device buffers of m*k and m*k/32
+ *                bytes (x_q_out 16-B aligned) that receive the quantized
+ *                activation (written by the workgroups of the first tile).
+ * Other arguments, effects and errors as mxgemm_publish. */
+int mxgemm_publish_bf16(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                        const uint16_t* x, int32_t m, int32_t n, int32_t k, int32_t split_k,
+                        void* workspace, size_t workspace_bytes, uint16_t* c_out,
+                        uint8_t* x_q_out, uint8_t* x_scale_out, void* stream);
+
+/* The plain GEMM without the publish: mxgemm_publish's product rounded to
+ * BF16 into `c_out` (required, [m, n], 16-B aligned), no mailbox touched.
+ * It is the first half of the unfused path the publishing_gemm page's
+ * module docstring describes (the GEMM writes its output, then a publish
+ * kernel reads it back into the mailbox; here mailbox_publish). Other
+ * arguments and errors as mxgemm_publish (no MXG_ECAPACITY). */
+int mxgemm(const uint8_t* w, const uint8_t* w_scale, const uint8_t* x, const uint8_t* x_scale,
+           int32_t m, int32_t n, int32_t k, int32_t split_k, void* workspace,
+           size_t workspace_bytes, uint16_t* c_out, void* stream);
+
+/* Stand-alone activation quantizer, the rule of mxgemm_publish_bf16:
+ * [rows, k] BF16 `x` (device, 16-B aligned) -> e4m3fn codes `x_q` ([rows,
+ * k], 16-B aligned) and E8M0 scales `x_scale` ([rows, k/32]). The unfused
+ * form of the quantizing step. Errors: MXG_EINVAL (null, rows < 1, k not a
+ * positive multiple of 32), MXG_EALIGN, MXG_EHIP. */
+int mxfp8_quantize(const uint16_t* x, int32_t rows, int32_t k, uint8_t* x_q, uint8_t* x_scale,
+                   void* stream);
+
 /* Unfused publish: copy `nbytes` of BF16 from `src` (device, 16-B aligned)
  * into slot `rank` with negative zero cleared. For the owner's slot
  * (rank == mb->rank) the generation is state[NEXT] and state[ACTIVE] is set;

@@ -97,6 +97,10 @@ def _load() -> ctypes.CDLL:
         "mailbox_collect": (ctypes.c_int, [mbp, vp, i64, vp]),
         "mailbox_collect_sum": (ctypes.c_int, [mbp, vp, i64, vp]),
         "mailbox_publish_words": (ctypes.c_int, [mbp, i32, vp, i64, vp]),
+        "mxgemm_publish_bf16": (ctypes.c_int, [mbp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp,
+                                               vp, vp, vp]),
+        "mxgemm": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp, vp]),
+        "mxfp8_quantize": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
         "mailbox_all_gather": (ctypes.c_int, [mbp, vp, vp, i64, vp]),
         "mxg_set_spin_limit": (u32, [u32]),
         "mxg_graph_begin": (ctypes.c_int, [vp]),
@@ -248,6 +252,27 @@ def mailbox_collect(mb: mxg_mailbox, out, nbytes: int, stream=None) -> None:
 def mailbox_collect_sum(mb: mxg_mailbox, out, nbytes: int, stream=None) -> None:
     _check(_lib.mailbox_collect_sum(ctypes.byref(mb), _ptr(out), nbytes, _stream(stream)),
            "mailbox_collect_sum")
+
+
+def mxgemm_publish_bf16(mb: mxg_mailbox, w, w_scale, x, m: int, n: int, k: int, split_k: int,
+                        workspace, workspace_bytes: int, c_out=None, x_q_out=None,
+                        x_scale_out=None, stream=None) -> None:
+    _check(_lib.mxgemm_publish_bf16(ctypes.byref(mb), _ptr(w), _ptr(w_scale), _ptr(x), m, n, k,
+                                    split_k, _ptr(workspace), workspace_bytes, _ptr(c_out),
+                                    _ptr(x_q_out), _ptr(x_scale_out), _stream(stream)),
+           "mxgemm_publish_bf16")
+
+
+def mxgemm(w, w_scale, x, x_scale, m: int, n: int, k: int, split_k: int, workspace,
+           workspace_bytes: int, c_out, stream=None) -> None:
+    _check(_lib.mxgemm(_ptr(w), _ptr(w_scale), _ptr(x), _ptr(x_scale), m, n, k, split_k,
+                       _ptr(workspace), workspace_bytes, _ptr(c_out), _stream(stream)),
+           "mxgemm")
+
+
+def mxfp8_quantize(x, rows: int, k: int, x_q, x_scale, stream=None) -> None:
+    _check(_lib.mxfp8_quantize(_ptr(x), rows, k, _ptr(x_q), _ptr(x_scale), _stream(stream)),
+           "mxfp8_quantize")
 
 
 def mailbox_publish_words(mb: mxg_mailbox, rank: int, src, nbytes: int, stream=None) -> None:

@@ -97,18 +97,27 @@ int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
 }
 
 namespace {
-int publish_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
-                 const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n, int32_t k,
-                 int32_t split_k, void* workspace, size_t workspace_bytes, uint16_t* c_out,
-                 void* stream, void* ev_start, void* ev_stop) {
-  if (!mailbox_ok(mb) || !w || !w_scale || !x || !x_scale) return MXG_EINVAL;
+// One GEMM launch. mb null: plain GEMM into c_out (required). xb non-null:
+// BF16 x quantized in the kernel (x and x_scale must be null), with the
+// quantized activation optionally written to xq_out / xs_out.
+int gemm_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+              const uint8_t* x, const uint8_t* x_scale, const uint16_t* xb, int32_t m, int32_t n,
+              int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
+              uint16_t* c_out, uint8_t* xq_out, uint8_t* xs_out, void* stream, void* ev_start,
+              void* ev_stop) {
+  if (mb ? !mailbox_ok(mb) : !c_out) return MXG_EINVAL;
+  if (!w || !w_scale) return MXG_EINVAL;
+  if (xb ? (x || x_scale) : (!x || !x_scale || xq_out || xs_out)) return MXG_EINVAL;
+  if (xb && (!xq_out) != (!xs_out)) return MXG_EINVAL;
   if (m < 1 || m > MXG_MAX_ROWS || n <= 0 || n % 8 || k <= 0 || k % 128) return MXG_EINVAL;
   if (split_k != 1 && split_k != 2 && split_k != 4 && split_k != 8) return MXG_EINVAL;
   if (k % (128 * split_k)) return MXG_EINVAL;
-  if (!aligned16(w) || !aligned16(w_scale) || !aligned16(x) || !aligned16(x_scale) ||
-      !aligned16(mb->slots) || !aligned16(mb->state) || (c_out && !aligned16(c_out)))
+  if (!aligned16(w) || !aligned16(w_scale) || (x && !aligned16(x)) ||
+      (x_scale && !aligned16(x_scale)) || (xb && !aligned16(xb)) ||
+      (xq_out && !aligned16(xq_out)) || (c_out && !aligned16(c_out)))
     return MXG_EALIGN;
-  if ((int64_t)2 * m * n > mb->capacity_bytes) return MXG_ECAPACITY;
+  if (mb && (!aligned16(mb->slots) || !aligned16(mb->state))) return MXG_EALIGN;
+  if (mb && (int64_t)2 * m * n > mb->capacity_bytes) return MXG_ECAPACITY;
   if (split_k > 1) {
     if (!workspace || workspace_bytes < mxgemm_workspace_bytes(m, n, k, split_k))
       return MXG_EWORKSPACE;
@@ -126,9 +135,13 @@ int publish_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale
   a.ws = w_scale;
   a.x = x;
   a.xs = x_scale;
-  a.slot = static_cast<uint8_t*>(mb->slots) + (size_t)mb->rank * mb->capacity_bytes;
-  a.gen_stride = (int64_t)mb->ranks * mb->capacity_bytes;
-  a.state = mb->state;
+  a.xb = xb;
+  a.xq_out = xq_out;
+  a.xs_out = xs_out;
+  a.slot = mb ? static_cast<uint8_t*>(mb->slots) + (size_t)mb->rank * mb->capacity_bytes
+              : nullptr;
+  a.gen_stride = mb ? (int64_t)mb->ranks * mb->capacity_bytes : 0;
+  a.state = mb ? mb->state : nullptr;
   a.ws_hdr = split_k > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
   a.flags = split_k > 1 ? static_cast<uint32_t*>(workspace) + MXG_WS_HEADER_BYTES / 4 : nullptr;
   a.pairs = split_k > 1 ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
@@ -154,17 +167,42 @@ int mxgemm_publish(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_sca
                    const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n, int32_t k,
                    int32_t split_k, void* workspace, size_t workspace_bytes, uint16_t* c_out,
                    void* stream) {
-  return publish_impl(mb, w, w_scale, x, x_scale, m, n, k, split_k, workspace, workspace_bytes,
-                      c_out, stream, nullptr, nullptr);
+  if (!mb) return MXG_EINVAL;
+  return gemm_impl(mb, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
+                   workspace_bytes, c_out, nullptr, nullptr, stream, nullptr, nullptr);
 }
 
 int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
                          const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n,
                          int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
                          uint16_t* c_out, void* stream, void* ev_start, void* ev_stop) {
-  if (!ev_start || !ev_stop) return MXG_EINVAL;
-  return publish_impl(mb, w, w_scale, x, x_scale, m, n, k, split_k, workspace, workspace_bytes,
-                      c_out, stream, ev_start, ev_stop);
+  if (!mb || !ev_start || !ev_stop) return MXG_EINVAL;
+  return gemm_impl(mb, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
+                   workspace_bytes, c_out, nullptr, nullptr, stream, ev_start, ev_stop);
+}
+
+int mxgemm_publish_bf16(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                        const uint16_t* x, int32_t m, int32_t n, int32_t k, int32_t split_k,
+                        void* workspace, size_t workspace_bytes, uint16_t* c_out,
+                        uint8_t* x_q_out, uint8_t* x_scale_out, void* stream) {
+  if (!mb || !x) return MXG_EINVAL;
+  return gemm_impl(mb, w, w_scale, nullptr, nullptr, x, m, n, k, split_k, workspace,
+                   workspace_bytes, c_out, x_q_out, x_scale_out, stream, nullptr, nullptr);
+}
+
+int mxgemm(const uint8_t* w, const uint8_t* w_scale, const uint8_t* x, const uint8_t* x_scale,
+           int32_t m, int32_t n, int32_t k, int32_t split_k, void* workspace,
+           size_t workspace_bytes, uint16_t* c_out, void* stream) {
+  if (!c_out) return MXG_EINVAL;
+  return gemm_impl(nullptr, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
+                   workspace_bytes, c_out, nullptr, nullptr, stream, nullptr, nullptr);
+}
+
+int mxfp8_quantize(const uint16_t* x, int32_t rows, int32_t k, uint8_t* x_q, uint8_t* x_scale,
+                   void* stream) {
+  if (!x || !x_q || !x_scale || rows < 1 || k <= 0 || k % 32) return MXG_EINVAL;
+  if (!aligned16(x) || !aligned16(x_q)) return MXG_EALIGN;
+  return hip_code(launch_quantize(x, rows, k, x_q, x_scale, static_cast<hipStream_t>(stream)));
 }
 
 namespace {

@@ -55,6 +55,7 @@
 
 #include "../../include/mxgemm.h"
 #include "mxgemm_internal.h"
+#include "quant_device.h"
 
 namespace mxg {
 namespace {
@@ -176,6 +177,76 @@ struct XStage {
 };
 
 
+// Quantizing activation stage: BF16 x of the workgroup's K slice becomes
+// e4m3 codes and E8M0 scales in LDS, in the layout XStage writes (the codes
+// of 16-value chunk (t, q) at XStage::dest, scale byte (t, b) at t*KS/32 + b).
+// Each thread loads 16-byte chunks of 8 BF16 values; chunk c of the slice
+// is row t = c / cpr8, values 8q .. 8q+7 with q = c % cpr8, so the 4 chunks
+// of a 32-value block are 4 consecutive lanes (cpr8 and the round size are
+// multiples of 4). Indices past the slice re-read the last chunk and are
+// not stored; whole blocks lie on either side of that bound. A wave whose
+// chunks of a round all lie past the slice skips them (loads and
+// arithmetic); the test is on the wave's first chunk, so it is uniform. With
+// q_out the codes and scales also go to [m, K] and [m, K/32] in global
+// memory.
+template <int NT>
+struct XQuant {
+  static constexpr int kChunks = 8;  // chunks per thread per round
+  uint4 v[kChunks];
+
+  __device__ __forceinline__ void load(const uint16_t* xb, int K, size_t k0, int cpr8,
+                                       int xch8, int c0, int tid) {
+    const int wbase = tid & ~63;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      if (c0 + i * NT + wbase >= xch8) break;
+      int c = c0 + i * NT + tid;
+      c = c < xch8 ? c : xch8 - 1;
+      const int t = c / cpr8;
+      const int q = c - t * cpr8;
+      v[i] = *reinterpret_cast<const uint4*>(xb + (size_t)t * K + k0 + 8 * q);
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* xlb, uint8_t* xsl, int K, size_t k0, int m,
+                                        int cpr8, int xch8, int c0, int tid, uint8_t* q_out,
+                                        uint8_t* s_out) const {
+    const int cpr = cpr8 >> 1;
+    const int kspw = cpr8 >> 2;
+    const int wbase = tid & ~63;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      if (c0 + i * NT + wbase >= xch8) break;
+      const int c = c0 + i * NT + tid;
+      const uint32_t sb = block_scale_byte(quad_max(chunk_amax(v[i])));
+      const uint2 codes = chunk_codes(v[i], sb);
+      if (c < xch8) {
+        const int t = c / cpr8;
+        const int q = c - t * cpr8;
+        const int d = XStage<NT>::dest(t * cpr + (q >> 1), cpr, m);
+        *reinterpret_cast<uint2*>(xlb + (size_t)d * 16 + 8 * (q & 1)) = codes;
+        if ((q & 3) == 0) xsl[t * kspw + (q >> 2)] = (uint8_t)sb;
+        if (q_out) {
+          *reinterpret_cast<uint2*>(q_out + (size_t)t * K + k0 + 8 * q) = codes;
+          if ((q & 3) == 0) s_out[(size_t)t * (K >> 5) + (k0 >> 5) + (q >> 2)] = (uint8_t)sb;
+        }
+      }
+    }
+  }
+};
+
+// The quantizing rounds past the first (see stage_rest).
+template <int NT>
+__device__ __attribute__((noinline)) void quant_rest(const uint16_t* xb, int K, size_t k0, int m,
+                                                     int cpr8, int xch8, int tid, uint8_t* xlb,
+                                                     uint8_t* xsl, uint8_t* q_out,
+                                                     uint8_t* s_out) {
+  XQuant<NT> st;
+  for (int c0 = XQuant<NT>::kChunks * NT; c0 < xch8; c0 += XQuant<NT>::kChunks * NT) {
+    st.load(xb, K, k0, cpr8, xch8, c0, tid);
+    st.store(xlb, xsl, K, k0, m, cpr8, xch8, c0, tid, q_out, s_out);
+  }
+}
+
 // The rounds of x staging past the first, for slices larger than one round.
 // Kept out of line: its loads would otherwise make the compiler wait for every
 // W load in flight before the main loop of the common one-round case.
@@ -236,7 +307,9 @@ __global__ void pack_weight_kernel(const uint8_t* w, const uint8_t* ws, int n, i
 // in workgroup 0 advances the epoch once every workgroup has read it. No
 // worker wave waits for these round trips (loads and stores complete in
 // order per wave, so one in flight would hold the worker's W loads).
-template <int RB, int WN, int WK, int D, int SK>
+// QX: x arrives as BF16 (a.xb) and is quantized in the activation stage.
+// Without a mailbox (a.state null) the kernel is a plain GEMM into c_out.
+template <int RB, int WN, int WK, int D, int SK, bool QX>
 __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     __attribute__((amdgpu_waves_per_eu(2))) gemm_publish_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -287,7 +360,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   // loads are issued here and waited for only where the values are needed.
   uint32_t gen = 0, epoch = 0;
   if (tid == hand_tid) {
-    gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
+    if (a.state) gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
     if (S > 1) epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH);
   }
 
@@ -296,10 +369,17 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   const int xch = m * cpr;
   const int wpr = KS >> 7;  // x-scale words per token row in the slice
   const int nsw = m * wpr;
+  const int cpr8 = KS >> 3;  // 8-value BF16 chunks per x row (quantizing stage)
+  const int xch8 = m * cpr8;
   XStage<NT> xst;
+  XQuant<NT> xqs;
   if (!ctl) {
-    xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
-    xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
+    if constexpr (QX) {
+      xqs.load(a.xb, K, kslice0, cpr8, xch8, 0, tid);
+    } else {
+      xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
+      xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
+    }
   }
 
   // ---- W stream prologue (packed tiles, see mxgemm_pack_weight) ---------
@@ -321,14 +401,16 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   v4u wlo[D][RB], whi[D][RB];
   uint32_t wsc[D][RB];
   // Block j of this wave, or (j < 0) an in-bounds dummy: the first 128 bytes
-  // of x and the first scale word of xs, which every workgroup reads anyway.
-  // Every refill slot issues its loads either way, so the count of loads in
-  // flight is the same on every path.
+  // of x and the first scale word of xs (of BF16 x when quantizing), which
+  // every workgroup reads anyway. Every refill slot issues its loads either
+  // way, so the count of loads in flight is the same on every path.
+  const uint8_t* xd = QX ? reinterpret_cast<const uint8_t*>(a.xb) : a.x;
+  const uint32_t* xsd = reinterpret_cast<const uint32_t*>(QX ? xd : a.xs);
   auto load_w = [&](int d, int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const uint8_t* t = j >= 0 ? wtile[i] + (size_t)j * 2048 : a.x + 16 * (lane & 7);
-      const uint32_t* sc = j >= 0 ? stile[i] + (size_t)j * 16 : reinterpret_cast<const uint32_t*>(a.xs);
+      const uint8_t* t = j >= 0 ? wtile[i] + (size_t)j * 2048 : xd + 16 * (lane & 7);
+      const uint32_t* sc = j >= 0 ? stile[i] + (size_t)j * 16 : xsd;
       wlo[d][i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(t));
       whi[d][i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(t + (j >= 0 ? 1024 : 0)));
       wsc[d][i] = *sc;
@@ -344,11 +426,22 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     // The x loads were issued first, so waiting for them leaves the W
     // prologue in flight: the W stream starts at once and x lands in one
     // round trip.
-    uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
-    xst.store(xl);
-    xst.store_scales(xsw);
-    if (xch > XStage<NT>::kChunks * NT || nsw > XStage<NT>::kWords * NT)
-      stage_rest<NT>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
+    if constexpr (QX) {
+      // The workgroups of tile 0 (one per K slice) also write the quantized
+      // activation out when asked.
+      uint8_t* qo = tile == 0 ? a.xq_out : nullptr;
+      uint8_t* so = tile == 0 ? a.xs_out : nullptr;
+      uint8_t* xlb = reinterpret_cast<uint8_t*>(xl);
+      xqs.store(xlb, xsl, K, kslice0, m, cpr8, xch8, 0, tid, qo, so);
+      if (xch8 > XQuant<NT>::kChunks * NT)
+        quant_rest<NT>(a.xb, K, kslice0, m, cpr8, xch8, tid, xlb, xsl, qo, so);
+    } else {
+      uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
+      xst.store(xl);
+      xst.store_scales(xsw);
+      if (xch > XStage<NT>::kChunks * NT || nsw > XStage<NT>::kWords * NT)
+        stage_rest<NT>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
+    }
   }
   if (S == 1 && tid == hand_tid) {
     hdr[0] = gen;
@@ -570,31 +663,35 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
         const uint4 raw = {pair, p1, p2, p3};
         const size_t off = ((size_t)t * N + row0 + 8 * jc) * 2;
         if (a.c_out) *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(a.c_out) + off) = raw;
-        uint4 clean;
-        clean.x = clear_negative_zero(raw.x);
-        clean.y = clear_negative_zero(raw.y);
-        clean.z = clear_negative_zero(raw.z);
-        clean.w = clear_negative_zero(raw.w);
-        *reinterpret_cast<uint4*>(slot + off) = clean;
+        if (a.slot) {
+          uint4 clean;
+          clean.x = clear_negative_zero(raw.x);
+          clean.y = clear_negative_zero(raw.y);
+          clean.z = clear_negative_zero(raw.z);
+          clean.w = clear_negative_zero(raw.w);
+          *reinterpret_cast<uint4*>(slot + off) = clean;
+        }
       }
     }
   }
 
   // Hand the generation to the consumer once per grid (publishing_gemm page,
   // epilog_warp: block 0, one thread, sets the active stage word).
-  if (blockIdx.x == 0 && tid == hand_tid) st_agent_u32(a.state + MXG_STATE_ACTIVE, gen);
+  if (a.state && blockIdx.x == 0 && tid == hand_tid) st_agent_u32(a.state + MXG_STATE_ACTIVE, gen);
 }
 
 // ---- variant table --------------------------------------------------------
 struct Variant {
   TileCfg cfg;
   int split_k;
-  const void* fn;
+  const void* fn;    // MXFP8 x
+  const void* fn_q;  // BF16 x, quantized in the activation stage
 };
 
-#define MXG_V(RB, WN, WK, D, SK) \
-  Variant{TileCfg{RB, WN, WK, D}, SK, \
-          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK>)}
+#define MXG_V(RB, WN, WK, D, SK)                                                     \
+  Variant{TileCfg{RB, WN, WK, D}, SK,                                                \
+          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, false>), \
+          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, true>)}
 #define MXG_VARIANT(RB, WN, WK, D) \
   MXG_V(RB, WN, WK, D, 1), MXG_V(RB, WN, WK, D, 2), MXG_V(RB, WN, WK, D, 4), \
       MXG_V(RB, WN, WK, D, 8)
@@ -722,14 +819,19 @@ long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes) {
   }
   const Variant* v = find_variant(c, split_k);
   if (!v) return -1;
-  int per_cu = 0, cus = 0;
-  if (lds_bytes > 64 * 1024 &&
-      hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
-          hipSuccess)
-    return -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, v->fn, tile_threads(c, split_k),
-                                                   lds_bytes) != hipSuccess)
-    return -1;
+  // Both activation forms of the variant: a shape gets one tile either way.
+  int per_cu = 1 << 30, cus = 0;
+  for (const void* fn : {v->fn, v->fn_q}) {
+    int n = 0;
+    if (lds_bytes > 64 * 1024 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
+            hipSuccess)
+      return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, tile_threads(c, split_k),
+                                                     lds_bytes) != hipSuccess)
+      return -1;
+    per_cu = n < per_cu ? n : per_cu;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return -1;
   const long r = (long)per_cu * cus;
@@ -756,15 +858,16 @@ hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t 
   const size_t lds = gemm_lds_bytes(c, a.m, a.k / a.split_k);
   GemmArgs args = a;
   args.xcd_groups = a.split_k > 1 && tiles % 8 == 0 ? 1 : 0;
+  const void* fn = a.xb ? v->fn_q : v->fn;
   if (lds > 64 * 1024) {
     const hipError_t e =
-        hipFuncSetAttribute(v->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   void* kargs[] = {&args};
   if (ev_start || ev_stop)
-    return hipExtLaunchKernel(v->fn, grid, block, kargs, lds, s, ev_start, ev_stop, 0);
-  return hipLaunchKernel(v->fn, grid, block, kargs, lds, s);
+    return hipExtLaunchKernel(fn, grid, block, kargs, lds, s, ev_start, ev_stop, 0);
+  return hipLaunchKernel(fn, grid, block, kargs, lds, s);
 }
 
 }  // namespace mxg

@@ -12,11 +12,14 @@ namespace mxg {
 struct GemmArgs {
   const uint8_t* w;   // packed W tiles (mxgemm_pack_weight)
   const uint8_t* ws;  // packed scales
-  const uint8_t* x;   // [m, k] e4m3fn
-  const uint8_t* xs;  // [m, k/32] E8M0
-  uint8_t* slot;      // mailbox slots + rank * capacity (generation 0)
+  const uint8_t* x;   // [m, k] e4m3fn (null when xb is given)
+  const uint8_t* xs;  // [m, k/32] E8M0 (null when xb is given)
+  const uint16_t* xb; // [m, k] BF16 to quantize in the kernel, or null
+  uint8_t* xq_out;    // with xb: [m, k] codes as quantized, or null
+  uint8_t* xs_out;    // with xb: [m, k/32] scales as quantized, or null
+  uint8_t* slot;      // mailbox slots + rank * capacity (generation 0); null: no publish
   int64_t gen_stride; // bytes between generations: ranks * capacity
-  uint32_t* state;    // mailbox state words
+  uint32_t* state;    // mailbox state words; null: plain GEMM into c_out
   uint32_t* ws_hdr;   // split-K workspace header (null when split_k == 1)
   uint32_t* flags;    // split-K per-workgroup epoch words (null when split_k == 1)
   uint64_t* pairs;    // split-K (value, epoch) pairs (null when split_k == 1)
@@ -61,6 +64,10 @@ hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t 
 // Packs row-major W and scales into the GEMM's tile layout.
 hipError_t launch_pack_weight(const uint8_t* w, const uint8_t* ws, int n, int k, uint8_t* wp,
                               uint8_t* wsp, hipStream_t s);
+
+// Stand-alone activation quantizer: [rows, k] BF16 -> codes and scales.
+hipError_t launch_quantize(const uint16_t* x, int rows, int k, uint8_t* xq, uint8_t* xs,
+                           hipStream_t s);
 
 // Mailbox kernels.
 hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);

@@ -107,7 +107,8 @@ E4M3_NAN = 0x7F
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """float64 values of uint16 BF16 bit patterns (exact)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return b.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # NaN patterns widen to NaN
+        return b.view(np.float32).astype(np.float64)
 
 
 def quantize_bf16(bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

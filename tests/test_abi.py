@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 20
+    assert len(names) == 23
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -144,3 +144,57 @@ def test_misc(mx):
     assert lib.mxgemm_workspace_init(None, 1024, None) == -1
     assert lib.mxgemm_workspace_init(4096, 1024, None) == -1  # below header + epoch words
     assert lib.mxgemm_workspace_init(4100, 8448, None) == -2
+
+
+def test_bf16_publish_validation(mx):
+    """mxgemm_publish_bf16: BF16 x required, the two quantized outputs given
+    together or not at all, the usual size, alignment and capacity rules."""
+    lib = mx.library()
+    mb = _mb(mx)
+
+    def call(**kw):
+        a = dict(w=4096, ws=4096, x=4096, m=1, n=256, k=512, s=1, wsp=None, wsn=0, c=None,
+                 q=None, qs=None)
+        a.update(kw)
+        return lib.mxgemm_publish_bf16(ctypes.byref(mb), a["w"], a["ws"], a["x"], a["m"],
+                                       a["n"], a["k"], a["s"], a["wsp"], a["wsn"], a["c"],
+                                       a["q"], a["qs"], None)
+
+    assert call(x=None) == -1
+    assert call(m=9) == -1
+    assert call(k=96) == -1
+    assert call(q=8192) == -1          # codes without scales
+    assert call(qs=8192) == -1         # scales without codes
+    assert call(x=4096 + 8) == -2
+    assert call(q=8192 + 8, qs=9000) == -2
+    assert call(n=512) == -3           # 2*m*n above the 512-byte slot
+    assert call(s=4) == -4
+    assert lib.mxgemm_publish_bf16(None, 4096, 4096, 4096, 1, 256, 512, 1, None, 0, None, None,
+                                   None, None) == -1
+
+
+def test_plain_gemm_validation(mx):
+    lib = mx.library()
+
+    def call(**kw):
+        a = dict(w=4096, ws=4096, x=4096, xs=4096, m=1, n=256, k=512, s=1, wsp=None, wsn=0,
+                 c=8192)
+        a.update(kw)
+        return lib.mxgemm(a["w"], a["ws"], a["x"], a["xs"], a["m"], a["n"], a["k"], a["s"],
+                          a["wsp"], a["wsn"], a["c"], None)
+
+    assert call(c=None) == -1          # the output is the only result
+    assert call(x=None) == -1
+    assert call(m=0) == -1
+    assert call(c=8200) == -2
+    assert call(s=2) == -4
+
+
+def test_quantize_validation(mx):
+    lib = mx.library()
+    assert lib.mxfp8_quantize(None, 1, 32, 4096, 8192, None) == -1
+    assert lib.mxfp8_quantize(4096, 0, 32, 4096, 8192, None) == -1
+    assert lib.mxfp8_quantize(4096, 1, 48, 4096, 8192, None) == -1
+    assert lib.mxfp8_quantize(4096, 1, 32, None, 8192, None) == -1
+    assert lib.mxfp8_quantize(4100, 1, 32, 4096, 8192, None) == -2
+    assert lib.mxfp8_quantize(4096, 1, 32, 4104, 8192, None) == -2

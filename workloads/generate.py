@@ -16,6 +16,8 @@ optional split-K). These generators stand in for it with seeded Gaussian data:
 * Peer payloads for emulated rank slots are BF16 bit patterns of Gaussians
   with about 1 % of halves forced to 0x8000 and some 32-bit words forced to
   0x80000000 (the Lamport sentinel), which the publish must turn into 0.
+* BF16 activations (for the in-GEMM quantizer) are the same Gaussians with
+  outlier channels, rounded to BF16 (nearest even).
 * All-gather payloads are uniform random 32-bit words with about 1 % set to
   the sentinel and 1 % to its near neighbours.
 
@@ -232,3 +234,23 @@ def word_payloads(seed: int, ranks: int, words: int) -> np.ndarray:
     idx = rng.choice(flat.size, size=hits, replace=False)
     flat[idx] = near[rng.integers(0, near.size, size=hits)]
     return out
+
+
+def bf16_bits(values: np.ndarray) -> np.ndarray:
+    """uint16 BF16 patterns of finite float32 values, nearest even (input
+    preparation: the activation the quantizer receives is BF16)."""
+    b = np.ascontiguousarray(values, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return b.astype(np.uint16)
+
+
+def bf16_activation(seed: int, m: int, k: int, dist: str = "outliers") -> np.ndarray:
+    """uint16 BF16 activation [m, k]: N(0, 1) values, with "outliers" 1 % of
+    the K channels (round(0.01 k) distinct indices) times 50 in every row,
+    the same recipe as the MXFP8 activations before quantization."""
+    rng = np.random.default_rng(seed ^ 0xBF16)
+    x = _gaussian(rng, (m, k), 1.0)
+    if dist == "outliers":
+        ch = rng.choice(k, size=max(1, round(0.01 * k)), replace=False)
+        x[:, ch] *= np.float32(50.0)
+    return bf16_bits(x)
