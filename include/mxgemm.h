@@ -105,10 +105,10 @@ typedef struct mxg_mailbox {
  * the arguments are invalid. */
 size_t mxg_mailbox_slots_bytes(int32_t ranks, int64_t capacity_bytes);
 
-/* Fill `mb` and arm the mailbox: every slot word becomes the sentinel,
- * NEXT = ACTIVE = COLLECT_ARR = ERROR = 0 (all_gather page,
- * LamportAllGather.__init__: the mailbox starts as the sentinel with a zero
- * state). Enqueues fill kernels on `stream`; call it at a quiescent point,
+/* Fill `mb` and arm the mailbox: every slot word becomes the sentinel and
+ * every state word 0 (NEXT, ACTIVE, COLLECT_ARR, ERROR and the peer
+ * counters; all_gather page, LamportAllGather.__init__: the mailbox starts as
+ * the sentinel with a zero state). Enqueues fill kernels on `stream`; call it at a quiescent point,
  * outside graph capture. Errors: MXG_EINVAL (null, ranks outside 1..8, rank
  * outside 0..ranks-1, capacity not a positive multiple of 16), MXG_EALIGN,
  * MXG_EHIP. */
