@@ -289,6 +289,21 @@ def gemm_only_ms(run: Runner, K: int) -> float:
     return run.graph_ms(lambda: [run.gemm(i) for i in range(K)], K, after=run.peers_and_collect)
 
 
+def stream_ms(run: Runner, K: int) -> tuple[float, int]:
+    """Per launch: a graph of K plain reads (mxg_stream_read) of the packed W
+    of the rotating copies, the same bytes the GEMM streams from HBM."""
+    import torch
+
+    nbytes = run.w[0][0].numel()
+    chunks = -(-nbytes // run.mx.STREAM_CHUNK_BYTES)
+    sink = torch.empty(chunks, dtype=torch.int32, device=run.w[0][0].device)
+    body = lambda: [run.mx.mxg_stream_read(run.w[i % run.copies][0], nbytes, sink, run.stream)
+                    for i in range(K)]
+    body()
+    torch.cuda.synchronize()
+    return run.graph_ms(body, K), nbytes
+
+
 def headline(args) -> int:
     import numpy as np
     import torch
@@ -327,6 +342,7 @@ def headline(args) -> int:
         eager_ms_step = e0.elapsed_time(e1) / K
         ext_ms = [a.elapsed_time(b) for a, b in kev]
         kern_ms = gemm_only_ms(run, K)
+        read_ms, read_bytes = stream_ms(run, K)
         # Timed region: the K whole steps captured once as a HIP graph.
         ms_step = run.graph_ms(lambda: [run.step(i) for i in range(K)], K)
         state_ok = run.state_ok()
@@ -379,6 +395,14 @@ def headline(args) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile(),
+        },
+        "stream_context": {
+            "what": "plain HBM read of one packed W copy (mxg_stream_read), graph of K launches "
+                    "over the same rotating copies: the achievable read rate at this size",
+            "bytes": read_bytes,
+            "us": round(read_ms * 1e3, 3),
+            "gbs": round(read_bytes / (read_ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(read_bytes / (read_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "state_ok": state_ok,
     }

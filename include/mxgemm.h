@@ -301,6 +301,18 @@ int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stre
  * aligned. Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY, MXG_EHIP. */
 int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream);
 
+/* Measurement aid, not a step of the method: a plain HBM read of `bytes`
+ * (a positive multiple of 16, at most 2^40) from device memory `src` (16-B
+ * aligned), nothing else. It measures what this device's HBM delivers to a
+ * pure read stream of that size, the context for the GEMM's roofline
+ * fraction. Each MXG_STREAM_CHUNK_BYTES chunk i (the last one may be short)
+ * is read by one workgroup, which stores the XOR of the chunk's
+ * little-endian 32-bit words into sink[i]; `sink` is device memory of
+ * ceil(bytes / MXG_STREAM_CHUNK_BYTES) words. Errors: MXG_EINVAL, MXG_EALIGN,
+ * MXG_EHIP. */
+#define MXG_STREAM_CHUNK_BYTES 32768
+int mxg_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Poll limit of the device spin loops (collect and split-K), in polls; the
  * loops back off with s_sleep between polls. Returns the previous limit.
  * A limit of 0 restores the default (2^20 polls). Process-wide. */

@@ -103,6 +103,7 @@ def _load() -> ctypes.CDLL:
         "mxfp8_quantize": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
         "mailbox_all_gather": (ctypes.c_int, [mbp, vp, vp, i64, vp]),
         "mxg_set_spin_limit": (u32, [u32]),
+        "mxg_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
         "mxg_graph_begin": (ctypes.c_int, [vp]),
         "mxg_graph_end": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "mxg_graph_launch": (ctypes.c_int, [vp, vp]),
@@ -283,6 +284,14 @@ def mailbox_publish_words(mb: mxg_mailbox, rank: int, src, nbytes: int, stream=N
 def mailbox_all_gather(mb: mxg_mailbox, src, out, nbytes: int, stream=None) -> None:
     _check(_lib.mailbox_all_gather(ctypes.byref(mb), _ptr(src), _ptr(out), nbytes,
                                    _stream(stream)), "mailbox_all_gather")
+
+
+STREAM_CHUNK_BYTES = 32768
+
+
+def mxg_stream_read(src, nbytes: int, sink, stream=None) -> None:
+    _check(_lib.mxg_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "mxg_stream_read")
 
 
 def mxg_set_spin_limit(polls: int) -> int:

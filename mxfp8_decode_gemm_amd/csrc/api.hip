@@ -270,6 +270,12 @@ int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* 
       spin_limit(), static_cast<hipStream_t>(stream)));
 }
 
+int mxg_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 || bytes > ((size_t)1 << 40)) return MXG_EINVAL;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return MXG_EALIGN;
+  return hip_code(launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 uint32_t mxg_set_spin_limit(uint32_t polls) {
   return g_spin_limit.exchange(polls == 0 ? (1u << 20) : polls);
 }

@@ -69,6 +69,10 @@ hipError_t launch_pack_weight(const uint8_t* w, const uint8_t* ws, int n, int k,
 hipError_t launch_quantize(const uint16_t* x, int rows, int k, uint8_t* xq, uint8_t* xs,
                            hipStream_t s);
 
+// Plain read stream of `bytes` (a multiple of 16): one checksum word per
+// MXG_STREAM_CHUNK_BYTES chunk into sink.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+
 // Mailbox kernels.
 hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);
 hipError_t launch_state_init(uint32_t* state, hipStream_t s);

@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -198,3 +198,15 @@ def test_quantize_validation(mx):
     assert lib.mxfp8_quantize(4096, 1, 32, None, 8192, None) == -1
     assert lib.mxfp8_quantize(4100, 1, 32, 4096, 8192, None) == -2
     assert lib.mxfp8_quantize(4096, 1, 32, 4104, 8192, None) == -2
+
+
+def test_stream_read_validation(mx):
+    lib = mx.library()
+    assert lib.mxg_stream_read(None, 64, 8192, None) == -1
+    assert lib.mxg_stream_read(4096, 0, 8192, None) == -1
+    assert lib.mxg_stream_read(4096, 24, 8192, None) == -1
+    assert lib.mxg_stream_read(4096, 64, None, None) == -1
+    assert lib.mxg_stream_read(4104, 64, 8192, None) == -2
+    assert lib.mxg_stream_read(4096, 64, 8194, None) == -2
+    with open(os.path.join(ROOT, "include", "mxgemm.h")) as f:
+        assert f"#define MXG_STREAM_CHUNK_BYTES {mx.STREAM_CHUNK_BYTES}" in f.read()
