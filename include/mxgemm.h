@@ -51,10 +51,11 @@ extern "C" {
 
 /* Mailbox state words (uint32). NEXT and ACTIVE are the stage words of the
  * publishing_gemm page's module docstring: [0] the generation the owner's
- * next publish writes and its next collect reads (advanced by the collect
- * that empties it), [1] the generation the owner's last publish wrote.
- * COLLECT_ARR counts collect workgroups (all_gather page, step 3: the last to
- * arrive advances the generation). ERROR is a sticky bit set: MXG_ERR_* below.
+ * next publish writes (advanced by the collect that empties it), [1] the
+ * generation the owner's last publish wrote, which the collect reads.
+ * COLLECT_ARR counts the fused all-gather's workgroups (all_gather page, step
+ * 3: the last to arrive advances the generation). ERROR is a sticky bit set:
+ * MXG_ERR_* below.
  *
  * PEER_GEN + r is the generation counter of emulated peer slot r (r other
  * than the owner's rank): every rank keeps its own counter and advances it
@@ -268,7 +269,9 @@ int mailbox_publish_words(const mxg_mailbox* mb, int32_t rank, const void* src,
  * Equivalent to mailbox_publish_words(mb, mb->rank, src) followed by
  * mailbox_collect, except that the caller's own slot is never written (the
  * same thread would store, reload and reset it: same end state). Peers
- * publish with mailbox_publish_words before or during the call. `src` and
+ * publish with mailbox_publish_words before or during the call. The call
+ * takes the place of the caller's publish and collect for that generation:
+ * nothing else may publish into the caller's own slot before it. `src` and
  * `out` are device memory, 16-B aligned; `out` holds ranks * nbytes bytes;
  * `src` may be exactly out + rank * nbytes (in place) and must not overlap
  * `out` otherwise. Spin limit and MXG_ERR_COLLECT_SPIN as mailbox_collect.
@@ -277,11 +280,14 @@ int mailbox_all_gather(const mxg_mailbox* mb, const void* src, void* out, int64_
                        void* stream);
 
 /* Collect (all_gather page, module docstring, step 2; _AllGatherKernel.kernel):
- * for every rank r and pack p < nbytes/16 of generation g = state[NEXT],
- * poll the pack until none of its four words is the sentinel, write it to
+ * for every rank r and pack p < nbytes/16 of generation g = state[ACTIVE]
+ * (the generation the owner's publish wrote: publishing_gemm page, module
+ * docstring, "Ordering", the consumer reads stage_state[1]), poll the pack
+ * until none of its four words is the sentinel, write it to
  * out + (r * nbytes + 16 p) (rank-major: [ranks*m, n] for an [m, n]
- * payload), and store the sentinel back. The last workgroup to finish sets
- * state[NEXT] = (g + 1) mod 3 (step 3). A pack still holding a sentinel after
+ * payload), and store the sentinel back; state[NEXT] becomes (g + 1) mod 3
+ * (step 3). The owner's publish (mxgemm_publish or mailbox_publish into slot
+ * mb->rank) must precede the collect on its stream. A pack still holding a sentinel after
  * the spin limit is copied as it is and MXG_ERR_COLLECT_SPIN is set in
  * state[ERROR]. `out` is device memory of ranks * nbytes bytes, 16-B aligned.
  * Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY, MXG_EHIP. */
@@ -291,7 +297,7 @@ int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stre
  * (publishing_gemm page, module docstring: the boundary all-reduce after the
  * row-parallel GEMM). The pages do not print its internals; this is the plain
  * meaning in FP32. For every pack p < nbytes/16 of generation g =
- * state[NEXT], each rank's pack is polled as in mailbox_collect, the eight
+ * state[ACTIVE], each rank's pack is polled as in mailbox_collect, the eight
  * BF16 values at each position are added in FP32 in ascending rank order,
  * and the sums are rounded once to BF16 (nearest even) into out + 16 p
  * ([m, n] BF16 for an [m, n] payload; a sum can round to negative zero).

@@ -118,13 +118,23 @@ __global__ void publish_kernel(uint8_t* slot, int64_t gen_stride, uint32_t* stat
 // Collect: one thread per (rank, pack), grid-stride. Every thread loads the
 // generation word together with its first pack in all three generations, so
 // when the payload is already there (the usual case) the collect costs one
-// round trip. Each workgroup counts itself once after its generation load has
-// returned (the count's operand depends on the loaded word); the last one to
-// arrive advances the generation at its end (all_gather page, step 3). No
-// workgroup of this launch can read the advanced value: every read returned
-// before its workgroup's count, and the advancing store follows the last one.
+// round trip.
 //
-// kGather fuses the caller's own publish (all_gather page, _AllGatherKernel):
+// The consumer of a publish takes the generation from state[ACTIVE], which
+// the owner's publish set before this kernel started (publishing_gemm page,
+// module docstring, "Ordering": the consumer reads stage_state[1] after the
+// producer completed), and sets state[NEXT] = generation + 1 mod 3. No
+// workgroup of this launch reads NEXT, so one store suffices and no
+// workgroup waits for the others: a count of arriving workgroups on one word
+// was measured to cost 0.6 us (28 workgroups) to 3 us (256).
+//
+// kGather is the fused all-gather, which has no producer before it: it reads
+// the generation from NEXT, and since its own workgroups read that word, the
+// last one to arrive advances it (all_gather page, step 3): each workgroup
+// counts itself once after its generation load has returned (the count's
+// operand depends on the loaded word), so no workgroup of the launch can read
+// the advanced value. It also fuses the caller's own publish
+// (all_gather page, _AllGatherKernel):
 // the items of rank `self` come from `src` with sentinel words sent as 0,
 // straight to the output. The own slot is left untouched: publishing into it
 // and polling it back would be the same thread storing, reloading and
@@ -137,7 +147,7 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
   const int64_t total = packs * ranks;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t graw = ld_agent_u32(state + MXG_STATE_NEXT);
+  const uint32_t graw = ld_agent_u32(state + (kGather ? MXG_STATE_NEXT : MXG_STATE_ACTIVE));
   uint64_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0, lo2 = 0, hi2 = 0;
   if (i0 < total && !(kGather && i0 / packs == self)) {
     const int64_t r = i0 / packs;
@@ -153,7 +163,7 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
   }
   const uint32_t gen = graw % MXG_GENERATIONS;
   uint32_t arrived = 0;
-  if (threadIdx.x == 0)
+  if (kGather && threadIdx.x == 0)
     arrived = __hip_atomic_fetch_add(state + MXG_STATE_COLLECT_ARR,
                                      1u + (graw == 0xFFFFFFFFu ? 1u : 0u), __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
@@ -201,8 +211,12 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
   if (timed_out)
     __hip_atomic_fetch_or(state + MXG_STATE_ERROR, MXG_ERR_COLLECT_SPIN, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0 && arrived == gridDim.x - 1u) {
-    st_agent_u32(state + MXG_STATE_COLLECT_ARR, 0u);
+  if (kGather) {
+    if (threadIdx.x == 0 && arrived == gridDim.x - 1u) {
+      st_agent_u32(state + MXG_STATE_COLLECT_ARR, 0u);
+      st_agent_u32(state + MXG_STATE_NEXT, (gen + 1u) % MXG_GENERATIONS);
+    }
+  } else if (blockIdx.x == 0 && threadIdx.x == 0) {
     st_agent_u32(state + MXG_STATE_NEXT, (gen + 1u) % MXG_GENERATIONS);
   }
 }
@@ -212,19 +226,14 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
 // ranks' first loads issued together with the generation word), its eight
 // BF16 values are added in FP32 in ascending rank order, the sums are rounded
 // once to BF16 (nearest even) into out + 16 p, and every rank's pack is reset
-// to the sentinel. Generation hand-off and timeout as in collect_kernel.
+// to the sentinel. Generation hand-off (from ACTIVE, NEXT set by one store)
+// and timeout as in collect_kernel.
 __global__ void collect_sum_kernel(uint8_t* slots, int64_t gen_stride, int64_t capacity,
                                    int ranks, uint32_t* state, uint8_t* out, int64_t nbytes,
                                    uint32_t spin_limit) {
   const int64_t packs = nbytes / MXG_PACK_BYTES;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const uint32_t graw = ld_agent_u32(state + MXG_STATE_NEXT);
-  const uint32_t gen = graw % MXG_GENERATIONS;
-  uint32_t arrived = 0;
-  if (threadIdx.x == 0)
-    arrived = __hip_atomic_fetch_add(state + MXG_STATE_COLLECT_ARR,
-                                     1u + (graw == 0xFFFFFFFFu ? 1u : 0u), __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t gen = ld_agent_u32(state + MXG_STATE_ACTIVE) % MXG_GENERATIONS;
   uint8_t* base = slots + (size_t)gen * gen_stride;
   bool timed_out = false;
   for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < packs; p += stride) {
@@ -282,10 +291,8 @@ __global__ void collect_sum_kernel(uint8_t* slots, int64_t gen_stride, int64_t c
   if (timed_out)
     __hip_atomic_fetch_or(state + MXG_STATE_ERROR, MXG_ERR_COLLECT_SPIN, __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0 && arrived == gridDim.x - 1u) {
-    st_agent_u32(state + MXG_STATE_COLLECT_ARR, 0u);
+  if (blockIdx.x == 0 && threadIdx.x == 0)
     st_agent_u32(state + MXG_STATE_NEXT, (gen + 1u) % MXG_GENERATIONS);
-  }
 }
 
 unsigned blocks_for(int64_t items) {
