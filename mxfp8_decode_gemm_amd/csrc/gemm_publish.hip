@@ -117,12 +117,13 @@ __device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
 // Copies x chunks (16 bytes) of the workgroup's K slice into LDS in the order
 // the MFMA B operand reads them: chunk (kb, half, group, t) holds
 // x[t][kb*128 + 64*half + 16*group .. +16).
-template <int NT>
+// XR scales the round: 4 * XR chunks per thread, all loaded up front.
+template <int NT, int XR = 1>
 struct XStage {
-  static constexpr int kChunks = 4;  // chunks per thread per round
-  static constexpr int kWords = 2;   // scale words per thread per round
-  uint4 v0, v1, v2, v3;
-  int d0, d1, d2, d3;
+  static constexpr int kChunks = 4 * XR;  // chunks per thread per round
+  static constexpr int kWords = 2;        // scale words per thread per round
+  uint4 v[kChunks];
+  int d[kChunks];
   uint32_t s0, s1;
   int e0, e1;
 
@@ -142,15 +143,16 @@ struct XStage {
   // compiler can wait for exactly these, not for the W loads issued later.
   __device__ __forceinline__ void load(const uint8_t* x, int K, size_t k0, int m, int cpr,
                                        int xch, int c0, int tid) {
-    const int c_0 = c0 + tid, c_1 = c0 + NT + tid, c_2 = c0 + 2 * NT + tid, c_3 = c0 + 3 * NT + tid;
-    v0 = src(x, K, k0, c_0 < xch ? c_0 : xch - 1, cpr);
-    v1 = src(x, K, k0, c_1 < xch ? c_1 : xch - 1, cpr);
-    v2 = src(x, K, k0, c_2 < xch ? c_2 : xch - 1, cpr);
-    v3 = src(x, K, k0, c_3 < xch ? c_3 : xch - 1, cpr);
-    d0 = c_0 < xch ? dest(c_0, cpr, m) : -1;
-    d1 = c_1 < xch ? dest(c_1, cpr, m) : -1;
-    d2 = c_2 < xch ? dest(c_2, cpr, m) : -1;
-    d3 = c_3 < xch ? dest(c_3, cpr, m) : -1;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = c0 + i * NT + tid;
+      v[i] = src(x, K, k0, c < xch ? c : xch - 1, cpr);
+    }
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int c = c0 + i * NT + tid;
+      d[i] = c < xch ? dest(c, cpr, m) : -1;
+    }
   }
   // Scale words: x_scale row t, word q of the slice -> LDS word t * wpr + q.
   __device__ __forceinline__ void load_scales(const uint8_t* xs, int K, size_t k0, int wpr,
@@ -169,10 +171,9 @@ struct XStage {
     if (e1 >= 0) xsw[e1] = s1;
   }
   __device__ __forceinline__ void store(uint4* xl) const {
-    if (d0 >= 0) xl[d0] = v0;
-    if (d1 >= 0) xl[d1] = v1;
-    if (d2 >= 0) xl[d2] = v2;
-    if (d3 >= 0) xl[d3] = v3;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i)
+      if (d[i] >= 0) xl[d[i]] = v[i];
   }
 };
 
@@ -250,16 +251,16 @@ __device__ __attribute__((noinline)) void quant_rest(const uint16_t* xb, int K, 
 // The rounds of x staging past the first, for slices larger than one round.
 // Kept out of line: its loads would otherwise make the compiler wait for every
 // W load in flight before the main loop of the common one-round case.
-template <int NT>
+template <int NT, int XR>
 __device__ __attribute__((noinline)) void stage_rest(const uint8_t* x, const uint8_t* xs, int K,
                                                      size_t k0, int m, int cpr, int xch, int wpr,
                                                      int nsw, int tid, uint4* xl, uint32_t* xsw) {
-  XStage<NT> st;
-  for (int c0 = XStage<NT>::kChunks * NT; c0 < xch; c0 += XStage<NT>::kChunks * NT) {
+  XStage<NT, XR> st;
+  for (int c0 = XStage<NT, XR>::kChunks * NT; c0 < xch; c0 += XStage<NT, XR>::kChunks * NT) {
     st.load(x, K, k0, m, cpr, xch, c0, tid);
     st.store(xl);
   }
-  for (int c0 = XStage<NT>::kWords * NT; c0 < nsw; c0 += XStage<NT>::kWords * NT) {
+  for (int c0 = XStage<NT, XR>::kWords * NT; c0 < nsw; c0 += XStage<NT, XR>::kWords * NT) {
     st.load_scales(xs, K, k0, wpr, nsw, c0, tid);
     st.store_scales(xsw);
   }
@@ -308,8 +309,10 @@ __global__ void pack_weight_kernel(const uint8_t* w, const uint8_t* ws, int n, i
 // worker wave waits for these round trips (loads and stores complete in
 // order per wave, so one in flight would hold the worker's W loads).
 // QX: x arrives as BF16 (a.xb) and is quantized in the activation stage.
+// XR: MXFP8 x staged in rounds of 4 * XR chunks per thread (the first round's
+// loads all go out before the W prologue).
 // Without a mailbox (a.state null) the kernel is a plain GEMM into c_out.
-template <int RB, int WN, int WK, int D, int SK, bool QX>
+template <int RB, int WN, int WK, int D, int SK, bool QX, int XR = 1>
 __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     __attribute__((amdgpu_waves_per_eu(2))) gemm_publish_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -371,7 +374,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   const int nsw = m * wpr;
   const int cpr8 = KS >> 3;  // 8-value BF16 chunks per x row (quantizing stage)
   const int xch8 = m * cpr8;
-  XStage<NT> xst;
+  XStage<NT, XR> xst;
   XQuant<NT> xqs;
   if (!ctl) {
     if constexpr (QX) {
@@ -439,8 +442,8 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
       uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
       xst.store(xl);
       xst.store_scales(xsw);
-      if (xch > XStage<NT>::kChunks * NT || nsw > XStage<NT>::kWords * NT)
-        stage_rest<NT>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
+      if (xch > XStage<NT, XR>::kChunks * NT || nsw > XStage<NT, XR>::kWords * NT)
+        stage_rest<NT, XR>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
     }
   }
   if (S == 1 && tid == hand_tid) {
@@ -692,6 +695,11 @@ struct Variant {
   Variant{TileCfg{RB, WN, WK, D}, SK,                                                \
           reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, false>), \
           reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, true>)}
+// The two-round x stage (xr = 2); BF16 x stages through XQuant either way.
+#define MXG_V2(RB, WN, WK, D, SK)                                                        \
+  Variant{TileCfg{RB, WN, WK, D, 2}, SK,                                                 \
+          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, false, 2>), \
+          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, true>)}
 #define MXG_VARIANT(RB, WN, WK, D) \
   MXG_V(RB, WN, WK, D, 1), MXG_V(RB, WN, WK, D, 2), MXG_V(RB, WN, WK, D, 4), \
       MXG_V(RB, WN, WK, D, 8)
@@ -702,11 +710,13 @@ const Variant kVariants[] = {
     MXG_VARIANT(1, 7, 1, 4), MXG_VARIANT(1, 7, 1, 3), MXG_VARIANT(1, 2, 2, 8),
     MXG_VARIANT(1, 4, 2, 8), MXG_VARIANT(2, 1, 4, 4), MXG_VARIANT(1, 8, 1, 8),
     MXG_VARIANT(2, 2, 2, 4),
+    MXG_V2(1, 4, 1, 3, 1), MXG_V2(1, 4, 1, 3, 2), MXG_V2(1, 4, 1, 3, 4), MXG_V2(1, 4, 1, 3, 8),
 };
 
 const Variant* find_variant(const TileCfg& c, int split_k) {
   for (const Variant& v : kVariants)
     if (v.cfg.rb == c.rb && v.cfg.wn == c.wn && v.cfg.wk == c.wk && v.cfg.depth == c.depth &&
+        v.cfg.xr == c.xr &&
         v.split_k == split_k)
       return &v;
   return nullptr;
@@ -760,10 +770,12 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out)
     return resident > 0 && tiles * split_k <= resident && tiles * split_k <= MXG_WS_MAX_GROUPS;
   };
   if (const char* env = std::getenv("MXG_TILE")) {
-    // Measurement override: exactly this variant, or no launch at all.
+    // Measurement override: exactly this variant ("rb,wn,wk,depth[,xr]"), or
+    // no launch at all.
     TileCfg c{};
-    if (std::sscanf(env, "%d,%d,%d,%d", &c.rb, &c.wn, &c.wk, &c.depth) != 4 || !fits(c))
-      return false;
+    const int got = std::sscanf(env, "%d,%d,%d,%d,%d", &c.rb, &c.wn, &c.wk, &c.depth, &c.xr);
+    if (got == 4) c.xr = 1;
+    if ((got != 4 && got != 5) || !fits(c)) return false;
     *out = c;
     return true;
   }
@@ -803,6 +815,15 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out)
       found = true;
     }
   }
+  // A slice of x that needs more than one staging round of 4 chunks per
+  // thread: the variant with a two-round first stage, when built and resident
+  // (on C3's m = 8, S = 4 shape it measured 17.5 -> 16.8 us).
+  if (found) {
+    const long chunks = (long)m * (ks / 16);
+    TileCfg c2 = *out;
+    c2.xr = 2;
+    if (chunks > 4L * 64 * out->wn * out->wk && fits(c2)) *out = c2;
+  }
   return found;
 }
 
@@ -811,7 +832,8 @@ long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes) {
   static std::map<std::tuple<int, int, int, int, int, size_t>, long> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  const auto key = std::make_tuple(dev, c.rb, c.wn, c.wk * 100 + c.depth, split_k, lds_bytes);
+  const auto key =
+      std::make_tuple(dev, c.rb, c.wn, c.wk * 100 + c.depth + 10000 * c.xr, split_k, lds_bytes);
   {
     std::lock_guard<std::mutex> g(mu);
     auto it = cache.find(key);

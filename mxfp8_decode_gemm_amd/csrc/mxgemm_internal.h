@@ -33,8 +33,10 @@ struct GemmArgs {
 // A workgroup computes an output tile of n_tile = 16 * rb * wn rows for one
 // K slice; its 64 * wn * wk threads form wn x wk waves (wn along rows, wk
 // along K); each wave keeps `depth` K-blocks of W loads in flight.
+// xr: rounds of 4 chunks per thread in the activation stage's first round.
 struct TileCfg {
   int rb, wn, wk, depth;
+  int xr = 1;
 };
 
 inline int tile_rows(const TileCfg& c) { return 16 * c.rb * c.wn; }
@@ -46,7 +48,7 @@ inline int tile_threads(const TileCfg& c, int split_k) {
 // Dynamic LDS bytes of a launch (x slice, its scales, the partial tile).
 size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice);
 
-// The tile for a problem; MXG_TILE="rb,wn,wk,depth" forces one variant (and
+// The tile for a problem; MXG_TILE="rb,wn,wk,depth[,xr]" forces one variant (and
 // fails when it does not fit). Returns false when no variant fits.
 bool choose_tile(int m, int n, int k, int split_k, TileCfg* out);
 
