@@ -14,9 +14,9 @@ from the 256 MiB Infinity Cache.
 The timed region is one replay of a HIP graph holding the K steps back to
 back (the decode loop as it is served); `value` is algorithmic bytes per step
 over the replay's time per step. The GEMM kernel's own time per launch comes
-from a graph of K back-to-back GEMM+publish launches, HIP events around its
-replay on the launch stream; the roofline compares algorithmic bytes per
-launch over it with the 8 TB/s HBM peak. Also printed: the same with one W
+from a graph of K back-to-back GEMM+publish launches, HIP events around each
+of three replays on the launch stream (the median); the roofline compares
+algorithmic bytes per launch over it with the 8 TB/s HBM peak. Also printed: the same with one W
 copy (Infinity-Cache warm), the events attached to each eager launch, the
 parity of the final output against the CPU oracle, and the oracle's own time
 on the host (cpu_baseline).
@@ -244,19 +244,21 @@ class Runner:
         self.gemm(i, ev)
         self.peers_and_collect()
 
-    def graph_ms(self, body, calls: int, after=None) -> float:
+    def graph_ms(self, body, calls: int, after=None, timed: int = 1) -> float:
         """Capture body() (which enqueues `calls` calls) once; replay it warm,
-        then once between two events on the stream (after() runs outside the
-        graph following each replay); returns ms per call of the timed
-        replay."""
+        then `timed` times, each between two events on the stream (after()
+        runs outside the graph following each replay); returns ms per call,
+        the median over the timed replays."""
+        import statistics
+
         mx, torch, s = self.mx, self.torch, self.stream
         g0, c0 = self.gemm_calls, self.collects
         mx.mxg_graph_begin(s)
         body()
         graph = mx.mxg_graph_end(s)
         dg, dc = self.gemm_calls - g0, self.collects - c0
-        ms = 0.0
-        for rep in range(2):
+        times = []
+        for rep in range(1 + timed):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(s)
@@ -265,12 +267,12 @@ class Runner:
             if after is not None:
                 after()
             torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1)
-            if rep == 1:  # the capture counted the first replay's calls
+            if rep > 0:  # the capture counted the warm replay's calls
+                times.append(e0.elapsed_time(e1))
                 self.gemm_calls += dg
                 self.collects += dc
         mx.mxg_graph_destroy(graph)
-        return ms / calls
+        return statistics.median(times) / calls
 
     def state_ok(self) -> bool:
         mx = self.mx
@@ -286,7 +288,8 @@ def gemm_only_ms(run: Runner, K: int) -> float:
     """Per launch: a graph of K back-to-back GEMM+publish launches (each
     republishes into the same generation); the emulated peers' publishes and a
     collect drain the mailbox after each replay."""
-    return run.graph_ms(lambda: [run.gemm(i) for i in range(K)], K, after=run.peers_and_collect)
+    return run.graph_ms(lambda: [run.gemm(i) for i in range(K)], K, after=run.peers_and_collect,
+                        timed=3)
 
 
 def stream_ms(run: Runner, K: int) -> tuple[float, int]:
@@ -301,7 +304,7 @@ def stream_ms(run: Runner, K: int) -> tuple[float, int]:
                     for i in range(K)]
     body()
     torch.cuda.synchronize()
-    return run.graph_ms(body, K), nbytes
+    return run.graph_ms(body, K, timed=3), nbytes
 
 
 def headline(args) -> int:
@@ -446,7 +449,7 @@ def all_configs(args) -> int:
                 run.step(i)
             torch.cuda.synchronize()
             kern_ms = gemm_only_ms(run, K)
-            step_ms = run.graph_ms(lambda: [run.step(i) for i in range(K)], K)
+            step_ms = run.graph_ms(lambda: [run.step(i) for i in range(K)], K, timed=3)
             ok = run.state_ok()
         del run
         torch.cuda.empty_cache()
@@ -659,8 +662,10 @@ def activation_quant(args) -> int:
             torch.cuda.synchronize()
             # kernels alone: K back-to-back calls, the mailbox drained after
             # each replay (every call republishes into the same generation)
-            kern_ms = run.graph_ms(lambda: [body(i) for i in range(K)], K, after=run.collect)
-            step_ms = run.graph_ms(lambda: [(body(i), run.collect()) for i in range(K)], K)
+            kern_ms = run.graph_ms(lambda: [body(i) for i in range(K)], K, after=run.collect,
+                                   timed=3)
+            step_ms = run.graph_ms(lambda: [(body(i), run.collect()) for i in range(K)], K,
+                                   timed=3)
             lines.append((name, calls, kern_ms, step_ms))
         state_ok = run.state_ok()
     algo = p.algorithmic_bytes()
