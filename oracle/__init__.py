@@ -12,11 +12,13 @@ computes, in float64 / exact integer arithmetic:
                    float64, negative-zero clearing of BF16 bits.
 * ``quant``     -- the per-32 MXFP8 quantizer (scale = smallest power of two that
                    brings the block into e4m3 range), used to pin the input
-                   generator.
+                   generator, and its BF16-input form for the activation
+                   quantizer in front of the GEMM.
 * ``gemm``      -- C[t, n] = sum_k dec(W[n,k]) 2^(Ws-127) dec(x[t,k]) 2^(xs-127)
                    in float64, its absolute-value sum, and the BF16 result.
 * ``mailbox``   -- the three-generation Lamport mailbox: publish, collect,
-                   reset, generation advance, and the invariant checker.
+                   reset, generation advance, and the invariant checker; the
+                   word publish and fused all-gather; the all-reduce collect.
 * ``tolerance`` -- the BF16 acceptance bound used by every parity test.
 
 Page citations in this package name the four API pages by module:
