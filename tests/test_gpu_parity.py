@@ -551,3 +551,40 @@ def test_config4_million_alternating_calls(env):
 
     probs = [generate.config_problem(4, size=s) for s in (0, 1)]
     graph_soak(env, probs, 4, 4, 32768, per_graph=1000, replays=1000, ws_n=7168)
+
+
+def test_publish_timed_matches_publish(env):
+    """mxgemm_publish_timed: the same output and mailbox effects as
+    mxgemm_publish, and its two events bracket the kernel (a positive duration
+    shorter than the host's wall time around the call)."""
+    import time
+
+    mx, dv = env
+    from workloads import generate
+
+    p = generate.random_problem(4242, 8, 2048, 4096, 4)
+    ops = dv.Operands(p)
+    ws = dv.Workspace(p.n, 4)
+    a, b = dv.Mailbox(1, p.out_bytes), dv.Mailbox(1, p.out_bytes)
+    ca = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
+    cb = torch.empty_like(ca)
+    dv.publish(a, ops, 4, ws, ca)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()  # materialize the handles
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    mx.mxgemm_publish_timed(b.mb, ops.w, ops.ws, ops.x, ops.xs, p.m, p.n, p.k, 4, ws.buf,
+                            ws.nbytes, cb, None, e0, e1)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    assert torch.equal(ca, cb)
+    assert np.array_equal(a.slot_words(), b.slot_words())
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < wall_ms
+    assert b.state_words()[mx.STATE_ACTIVE] == 0 and ws.header()[mx.WS_EPOCH] == 3
+    with pytest.raises(mx.MxgValueError):
+        mx.mxgemm_publish_timed(b.mb, ops.w, ops.ws, ops.x, ops.xs, p.m, p.n, p.k, 4, ws.buf,
+                                ws.nbytes, cb, None, None, e1)
