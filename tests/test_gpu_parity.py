@@ -588,3 +588,34 @@ def test_publish_timed_matches_publish(env):
     with pytest.raises(mx.MxgValueError):
         mx.mxgemm_publish_timed(b.mb, ops.w, ops.ws, ops.x, ops.xs, p.m, p.n, p.k, 4, ws.buf,
                                 ws.nbytes, cb, None, None, e1)
+
+
+def test_large_n_split_grid_rejected_and_plain_runs(env):
+    """Maximum sizes: a split-K grid that cannot be resident all at once (its
+    workgroups wait for each other) is refused before anything is enqueued,
+    leaving the mailbox untouched; the same shape without split-K runs and
+    matches the oracle."""
+    mx, dv = env
+    codecs, gemm, mailbox, tolerance = _oracle()
+    from workloads import generate
+
+    p = generate.random_problem(6553, 2, 65536, 1024, 8)
+    _say(f"case m={p.m} n={p.n} k={p.k} split_k=8 (expect refusal), then split_k=1")
+    ops = dv.Operands(p)
+    mbx = dv.Mailbox(1, p.out_bytes)
+    ws = dv.Workspace(p.n, 8)
+    torch.cuda.synchronize()
+    with pytest.raises(mx.MxgUnsupported):
+        dv.publish(mbx, ops, 8, ws)
+    torch.cuda.synchronize()
+    assert not mailbox.check_idle_slots(mbx.slot_words())
+    assert ws.header()[mx.WS_EPOCH] == 1
+    c = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
+    dv.publish(mbx, ops, 1, None, c)
+    got = dv.as_u16(dv.collect(mbx, p.out_bytes)).reshape(p.m, p.n)
+    torch.cuda.synchronize()
+    raw = dv.as_u16(c).reshape(p.m, p.n)
+    _, exact, abs_sum = gemm.gemm_publish_bits(p.w, p.ws, p.x, p.xs)
+    assert tolerance.within(raw, exact, abs_sum)
+    assert np.array_equal(got, codecs.clear_negative_zero(raw))
+    assert not mailbox.check_idle_slots(mbx.slot_words())
