@@ -87,14 +87,39 @@ KERNEL_SOURCES = [os.path.join(ROOT, "mxfp8_decode_gemm_amd", "csrc", f)
                   for f in ("gemm_publish.hip", "mxgemm_internal.h", "quant_device.h")]
 
 
+def strip_comments(src: str) -> str:
+    """C++ source without its comments and trailing blanks: what compiles."""
+    import re
+
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif src[i] == '"':  # string literal: copy through, escapes included
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return "\n".join(line.rstrip() for line in re.sub(r"\n\s*\n+", "\n", "".join(out)).split("\n"))
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 over the GEMM kernel's source files, in order."""
+    """SHA-256 over the GEMM kernel's source files without comments, in order
+    (a comment edit leaves the measured kernel as it was)."""
     import hashlib
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -24,25 +24,37 @@
 //     about 2^-25 of the largest in its 32-element K step. The path is HBM
 //     bound, so the 4x MFMA count and the conversions cost well under a tenth
 //     of the kernel's time.
-//   * W never touches LDS: each lane streams its two 16-byte pieces of every
-//     128-wide K block straight from HBM into VGPRs (one instruction reads 64
-//     contiguous bytes of each of 16 rows), `depth` K blocks ahead. Lane l
-//     holds row l % 16 and K = 16*(l/16) + 0..15 and 64 + 16*(l/16) + 0..15
-//     of the block; the BF16 MFMA pairs A and B elements by lane group and
-//     position (measured), so the B operand uses the same K split.
+//   * W never touches LDS: it is re-laid once (mxgemm_pack_weight) into 2 KiB
+//     tiles of 16 rows x 128 K, so that each wave instruction reads 1 KiB of
+//     contiguous HBM straight into VGPRs, `depth` K blocks ahead. Lane l holds
+//     row l % 16 and K = 16*(l/16) + 0..15 and 64 + 16*(l/16) + 0..15 of the
+//     block; the BF16 MFMA pairs A and B elements by lane group and position
+//     (measured), so the B operand uses the same K split.
 //   * x and its scales for the workgroup's K slice are staged once in LDS, in
-//     the order the B operand reads them, and shared by every wave.
-//   * The waves of a workgroup split its K slice; their partial tiles meet in
-//     LDS and are summed in ascending K order.
-//   * Split-K across workgroups: every tile pack (8 columns of one token) has
-//     one owner slice (pack index mod split_k). The other slices store their
-//     partial pack as eight (FP32 bits, epoch) 64-bit pairs with agent-scope
-//     stores; the owner polls all of its pairs in one batch until every tag
-//     equals this launch's epoch (sync page = vllm.models.deepseek_v41.amd.
-//     mono.common.sync, Mailbox: one round trip, no drain, no flag), then
-//     sums the slices in ascending K order.
-//   * One thread owns one pack, so the eight BF16 values leave as one aligned
-//     16-byte store, with no cross-lane shuffle.
+//     the order the B operand reads them, and shared by every wave; their
+//     loads go out before the W prologue and are waited for after it (XR sets
+//     how many chunks each thread loads in that first round). With BF16 x
+//     (QX) the stage quantizes it to e4m3 codes and E8M0 scales on the way
+//     (quant_device.h).
+//   * A workgroup's worker waves split its rows (WN) and its K slice (WK);
+//     their partial tiles meet in LDS and are summed in ascending K order.
+//   * Split-K across workgroups: in every token row of a tile, slice s owns
+//     the contiguous pack columns [ceil(s P / S), ceil((s + 1) P / S)) (P packs
+//     per row). The other slices store their partials of those columns as
+//     (FP32 bits, epoch) 64-bit pairs with agent-scope stores; the owner's
+//     poll waves, which have no store of their own in flight, poll all of a
+//     column's pairs in one batch until every tag equals this launch's epoch
+//     (sync page = vllm.models.deepseek_v41.amd.mono.common.sync, Mailbox: one
+//     round trip, no drain, no flag), then sum the slices in ascending K order.
+//   * One lane per owned column rounds its sum to BF16; lane shuffles gather
+//     eight consecutive columns of one token into one lane, which writes one
+//     aligned 16-byte pack (and the raw pack to c_out when asked).
+//   * With split-K a control wave runs beside the workers: it reads the
+//     generation and the epoch, stores the epoch into this workgroup's word,
+//     and in workgroup 0 stores the next epoch once every word holds the
+//     current one, so no worker waits on those round trips.
+//   * Without a mailbox (state null) the kernel is the plain GEMM into c_out,
+//     the first half of the unfused publish path.
 
 #include <hip/hip_runtime.h>
 
