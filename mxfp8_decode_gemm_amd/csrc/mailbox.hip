@@ -1,20 +1,25 @@
-// Mailbox kernels: arm, unfused publish and collect of the three-generation
-// Lamport mailbox, for gfx950.
+// Mailbox kernels for gfx950: arm, unfused publish, the collects (rank-major
+// copy, all-reduce) and the fused all-gather of the three-generation Lamport
+// mailbox.
 //
 // all_gather page = the API page of
 // vllm.models.deepseek_v41.nvidia.ops.cute_dsl.all_gather. Its module
 // docstring (steps 1-3) and _AllGatherKernel.kernel define the protocol this
 // file implements for emulated rank slots on one GPU:
 //   * idle words hold the sentinel 0x80000000;
-//   * a publish writes a rank's payload into its slot of the current
-//     generation (here with BF16 negative zero cleared, which also keeps the
-//     sentinel word out of every payload);
+//   * a publish writes a rank's payload into its slot of a generation (here
+//     with BF16 negative zero cleared, which also keeps the sentinel word out
+//     of every payload): the owner's slot in generation NEXT, an emulated
+//     peer's slot in that peer's own counter PEER_GEN[r];
 //   * a collect polls each 16-byte pack of every rank's slot until none of
-//     its words is the sentinel, copies it out rank-major, stores the
-//     sentinel back, and the last workgroup to arrive advances the
-//     generation mod 3.
-// The all-gather variant (same module docstring, step 1) moves arbitrary
-// 32-bit words: a word equal to the sentinel goes out as 0, every other word
+//     its words is the sentinel, copies it out rank-major (or sums it), and
+//     stores the sentinel back; it takes the generation from ACTIVE, which
+//     the owner's publish set (publishing_gemm page, "Ordering"), and sets
+//     NEXT to the next one mod 3;
+//   * the fused all-gather reads NEXT itself, and the last of its workgroups
+//     to arrive advances it.
+// The all-gather moves arbitrary 32-bit words (same module docstring, step
+// 1): a word equal to the sentinel goes out as 0, every other word
 // unchanged. All payload traffic moves as 32-bit integers, never through
 // float registers (sync page, Mailbox.put_words: a NaN bit pattern would not
 // survive a float move).
