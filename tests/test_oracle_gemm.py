@@ -19,21 +19,26 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def _exact(w, ws, x, xs):
-    """C[t][n] as exact Fractions, summed term by term."""
+    """(C, S): C[t][n] = sum of the products and S[t][n] = sum of their
+    magnitudes, as exact Fractions summed term by term."""
     m, k = x.shape
     n = w.shape[0]
     out = [[Fraction(0)] * n for _ in range(m)]
+    mag = [[Fraction(0)] * n for _ in range(m)]
     for t in range(m):
         for j in range(n):
             acc = Fraction(0)
+            acc_abs = Fraction(0)
             for kk in range(k):
                 a = Fraction(codecs.e4m3_value(int(w[j, kk]))) * Fraction(
                     codecs.e8m0_value(int(ws[j, kk // 32])))
                 b = Fraction(codecs.e4m3_value(int(x[t, kk]))) * Fraction(
                     codecs.e8m0_value(int(xs[t, kk // 32])))
                 acc += a * b
+                acc_abs += abs(a * b)
             out[t][j] = acc
-    return out
+            mag[t][j] = acc_abs
+    return out, mag
 
 
 @pytest.mark.parametrize("m,n,k,seed", [(1, 8, 32, 1), (3, 16, 64, 2), (8, 16, 128, 3),
@@ -41,10 +46,13 @@ def _exact(w, ws, x, xs):
 def test_brute_force_exact_rationals(m, n, k, seed):
     p = generate.random_problem(seed, m, n, k)
     c, abs_sum = gemm.gemm_f64(p.w, p.ws, p.x, p.xs)
-    exact = _exact(p.w, p.ws, p.x, p.xs)
+    exact, mag = _exact(p.w, p.ws, p.x, p.xs)
     ex = np.array([[float(v) for v in row] for row in exact])
-    assert c.shape == (m, n)
-    assert np.all(np.abs(c - ex) <= 2.0**-50 * abs_sum + 1e-300)
+    ex_abs = np.array([[float(v) for v in row] for row in mag])
+    assert c.shape == (m, n) and abs_sum.shape == (m, n)
+    assert np.all(np.abs(c - ex) <= 2.0**-50 * ex_abs + 1e-300)
+    # The magnitude sum the acceptance bound is scaled by.
+    assert np.all(np.abs(abs_sum - ex_abs) <= 2.0**-50 * ex_abs)
     # Rounding the correctly rounded float64 of the exact value gives the
     # oracle's BF16 bits.
     assert np.array_equal(gemm.published_bits(c), gemm.published_bits(ex))
@@ -132,6 +140,20 @@ def test_zero_rows_publish_positive_zero():
     assert np.all(c[:, zr] == 0)
     assert np.all(bits[:, zr] == 0x0000)
     assert not np.any(bits == 0x8000)
+
+
+def test_published_bits_round_once_then_clear():
+    """The epilogue's bits of exact results, worked by hand: one rounding from
+    the exact value (not through FP32), ties to even, and negative zero
+    cleared after the rounding (a negative result too small for BF16 rounds
+    to -0 and is published as +0)."""
+    c = np.array([[1.0 + 2.0**-8 + 2.0**-30,   # above a tie: up (FP32 first would tie down)
+                   -(1.0 + 2.0**-8),            # a tie: to the even -1
+                   1.5 * 2.0**-133,             # between subnormal steps 1 and 2: even 2
+                   -(2.0**-140),                # rounds to -0, published as +0
+                   0.0, -3.0, 2.0**-126, 448.0]])
+    want = [0x3F81, 0xBF80, 0x0002, 0x0000, 0x0000, 0xC040, 0x0080, 0x43E0]
+    assert list(gemm.published_bits(c)[0]) == want
 
 
 def test_shapes_rejected():

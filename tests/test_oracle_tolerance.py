@@ -61,6 +61,21 @@ def test_two_steps_off_fails_unless_the_sum_allows_it():
     assert np.all(ex > 2.0) and np.all(ex < 4.0)
 
 
+def test_the_sum_term_is_one_millionth():
+    """The slack is exactly 1e-6 Sigma|W x| on top of one step: a value three
+    steps off passes once 1e-6 S reaches the error beyond one step, and fails
+    for S a hair smaller."""
+    exact = np.array([1.0 + 2.0**-9, -7.0 - 2.0**-6, 2.0**-100 * 1.3])
+    far = codecs.bf16_rne_bits(exact + 3 * np.sign(exact) * codecs.bf16_quantum(exact))
+    err = np.abs(codecs.bf16_to_f64(far) - exact)
+    need = (err - codecs.bf16_quantum(exact)) / 1e-6
+    assert np.all(need > 0)
+    for i in range(exact.size):
+        one = slice(i, i + 1)
+        assert tolerance.within(far[one], exact[one], need[one] * (1 + 1e-9))
+        assert not tolerance.within(far[one], exact[one], need[one] * (1 - 1e-9))
+
+
 def test_non_finite_device_values_always_fail():
     exact = np.array([1.0, -2.0, 0.0])
     for bits in (0x7FC0, 0x7F80, 0xFF80):
