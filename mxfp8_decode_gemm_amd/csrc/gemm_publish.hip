@@ -12,7 +12,8 @@
 //
 // How it is laid out on CDNA4 (not the pages' Blackwell design):
 //   * Numerics. W is the MFMA A operand (16 output rows per instruction), x
-//     the B operand (16 token columns; tokens >= m are zero). Each e4m3 byte
+//     the B operand (16 token columns; columns >= m repeat token 0 and are
+//     never read, so no lane branches on its token). Each e4m3 byte
 //     is turned, with its E8M0 scale, into the exact BF16 value
 //     dec(byte) * 2^(scale-127) by v_cvt_scalef32_pk_bf16_fp8, and the
 //     contraction runs on v_mfma_f32_16x16x32_bf16 with FP32 accumulation.
@@ -81,7 +82,9 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 // 2^(s-127) as an FP32 multiplier: the biased exponent s in the exponent
 // field; s == 0 is the subnormal 2^-127.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  return __uint_as_float(s ? (s << 23) : 0x00400000u);
+  // 2^-127 (an FP32 subnormal, kept: the library is built with FP32
+  // denormals on) times 2^s, one instruction; s = 255 gives +inf.
+  return __builtin_amdgcn_ldexpf(__uint_as_float(0x00400000u), (int)s);
 }
 
 // Eight e4m3fn bytes (two dwords, lowest byte first) times a power-of-two
@@ -334,8 +337,10 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const bool ctl = tid >= NT;           // the control wave (split-K only)
+  // Wave-uniform in a scalar register, so the W stream's base addresses and
+  // the per-block selects stay on the scalar unit.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool ctl = wave >= NT / 64;     // the control wave (split-K only)
   const int hand_tid = SK > 1 ? NT : 0; // reads the hand-off words
   const int wn = wave % WN;
   const int wk = wave / WN;
@@ -501,25 +506,25 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
 #pragma unroll
   for (int i = 0; i < RB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   const bool tok = r16 < m;
+  const int xrow = tok ? r16 : 0;  // x row this lane's B operand reads
   const int kspw = KS >> 5;  // scale bytes per x row in the slice
   const int sb0 = grp >> 1;  // 32-block of this lane's first 16 K (its second is sb0 + 2)
   auto consume = [&](int d, int j) __attribute__((always_inline)) {
     const int kb = kb_lo + j;  // K block within the slice
     // B operand: x of this lane's token as exact BF16, four K steps.
+    // Lanes past the last token convert token 0's values instead: the MFMA
+    // columns they feed are never read, and no lane branches.
     v8bf bx[4];
-    if (tok) {
-      const uint4 xlo = xl[((kb * 2 + 0) * 4 + grp) * m + r16];
-      const uint4 xhi = xl[((kb * 2 + 1) * 4 + grp) * m + r16];
-      const uint8_t* xsr = xsl + r16 * kspw + kb * 4;
+    {
+      const uint4 xlo = xl[((kb * 2 + 0) * 4 + grp) * m + xrow];
+      const uint4 xhi = xl[((kb * 2 + 1) * 4 + grp) * m + xrow];
+      const uint8_t* xsr = xsl + xrow * kspw + kb * 4;
       const float fs0 = e8m0_to_f32(xsr[sb0]);
       const float fs1 = e8m0_to_f32(xsr[sb0 + 2]);
       bx[0] = fp8x8_to_bf16(xlo.x, xlo.y, fs0);
       bx[1] = fp8x8_to_bf16(xlo.z, xlo.w, fs0);
       bx[2] = fp8x8_to_bf16(xhi.x, xhi.y, fs1);
       bx[3] = fp8x8_to_bf16(xhi.z, xhi.w, fs1);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bx[q] = v8bf{};
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
