@@ -36,7 +36,10 @@
 //     loads go out before the W prologue and are waited for after it (XR sets
 //     how many chunks each thread loads in that first round). With BF16 x
 //     (QX) the stage quantizes it to e4m3 codes and E8M0 scales on the way
-//     (quant_device.h).
+//     (quant_device.h). Variants built with X16 store the slice as its
+//     exact BF16 values instead (each chunk converted with its scale byte on
+//     the way into LDS), so the waves read the B operand without converting
+//     it; the chooser takes them when the 2 m k_slice bytes fit.
 //   * A workgroup's worker waves split its rows (WN) and its K slice (WK);
 //     their partial tiles meet in LDS and are summed in ascending K order.
 //   * Split-K across workgroups: in every token row of a tile, slice s owns
@@ -133,12 +136,13 @@ __device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
 // the MFMA B operand reads them: chunk (kb, half, group, t) holds
 // x[t][kb*128 + 64*half + 16*group .. +16).
 // XR scales the round: 4 * XR chunks per thread, all loaded up front.
-template <int NT, int XR = 1>
+template <int NT, int XR = 1, bool X16 = false>
 struct XStage {
   static constexpr int kChunks = 4 * XR;  // chunks per thread per round
   static constexpr int kWords = 2;        // scale words per thread per round
   uint4 v[kChunks];
   int d[kChunks];
+  uint32_t sc[X16 ? kChunks : 1];  // X16: the scale byte of each chunk
   uint32_t s0, s1;
   int e0, e1;
 
@@ -147,6 +151,15 @@ struct XStage {
     const int q = c - t * cpr;
     const int kb = q >> 3, w8 = q & 7;
     return ((kb * 2 + (w8 >> 2)) * 4 + (w8 & 3)) * m + t;
+  }
+  // X16: the first of the two BF16 pieces of chunk c (the second is 4 m
+  // further): piece ((kb * 4 + 2h + part) * 4 + grp) * m + t holds the eight
+  // values MFMA step 2h + part of lane group grp reads in K block kb.
+  __device__ __forceinline__ static int dest16(int c, int cpr, int m) {
+    const int t = c / cpr;
+    const int q = c - t * cpr;
+    const int kb = q >> 3, w8 = q & 7;
+    return ((kb * 4 + 2 * (w8 >> 2)) * 4 + (w8 & 3)) * m + t;
   }
   __device__ __forceinline__ static uint4 src(const uint8_t* x, int K, size_t k0, int c, int cpr) {
     const int t = c / cpr;
@@ -166,7 +179,19 @@ struct XStage {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int c = c0 + i * NT + tid;
-      d[i] = c < xch ? dest(c, cpr, m) : -1;
+      d[i] = c < xch ? (X16 ? dest16(c, cpr, m) : dest(c, cpr, m)) : -1;
+    }
+  }
+  // X16: the E8M0 byte of each chunk's 32-value block (two chunks per block).
+  __device__ __forceinline__ void load_chunk_scales(const uint8_t* xs, int K, size_t k0, int cpr,
+                                                    int xch, int c0, int tid) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      int c = c0 + i * NT + tid;
+      c = c < xch ? c : xch - 1;
+      const int t = c / cpr;
+      const int q = c - t * cpr;
+      sc[i] = xs[(size_t)t * (K >> 5) + (k0 >> 5) + (q >> 1)];
     }
   }
   // Scale words: x_scale row t, word q of the slice -> LDS word t * wpr + q.
@@ -185,10 +210,28 @@ struct XStage {
     if (e0 >= 0) xsw[e0] = s0;
     if (e1 >= 0) xsw[e1] = s1;
   }
-  __device__ __forceinline__ void store(uint4* xl) const {
+  // X16: keeps the scale conversion where it is called. Without it the
+  // compiler decodes the scale bytes right after their loads, and so waits
+  // for them before the W prologue is issued.
+  __device__ __forceinline__ void pin_scales() {
+    if constexpr (X16) {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i)
-      if (d[i] >= 0) xl[d[i]] = v[i];
+      for (int i = 0; i < kChunks; ++i) asm volatile("" : "+v"(sc[i]));
+    }
+  }
+  // FP8 chunks as they are, or (X16) as two pieces of exact BF16 values.
+  __device__ __forceinline__ void store(uint4* xl, int m) const {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      if (d[i] < 0) continue;
+      if constexpr (X16) {
+        const float fs = e8m0_to_f32(sc[i]);
+        xl[d[i]] = __builtin_bit_cast(uint4, fp8x8_to_bf16(v[i].x, v[i].y, fs));
+        xl[d[i] + 4 * m] = __builtin_bit_cast(uint4, fp8x8_to_bf16(v[i].z, v[i].w, fs));
+      } else {
+        xl[d[i]] = v[i];
+      }
+    }
   }
 };
 
@@ -205,7 +248,7 @@ struct XStage {
 // arithmetic); the test is on the wave's first chunk, so it is uniform. With
 // q_out the codes and scales also go to [m, K] and [m, K/32] in global
 // memory.
-template <int NT>
+template <int NT, bool X16 = false>
 struct XQuant {
   static constexpr int kChunks = 8;  // chunks per thread per round
   uint4 v[kChunks];
@@ -238,9 +281,16 @@ struct XQuant {
       if (c < xch8) {
         const int t = c / cpr8;
         const int q = c - t * cpr8;
-        const int d = XStage<NT>::dest(t * cpr + (q >> 1), cpr, m);
-        *reinterpret_cast<uint2*>(xlb + (size_t)d * 16 + 8 * (q & 1)) = codes;
-        if ((q & 3) == 0) xsl[t * kspw + (q >> 2)] = (uint8_t)sb;
+        if constexpr (X16) {
+          // The codes' exact BF16 values: one piece (see XStage::dest16).
+          const int d = XStage<NT, 1, true>::dest16(t * cpr + (q >> 1), cpr, m) + 4 * m * (q & 1);
+          reinterpret_cast<uint4*>(xlb)[d] =
+              __builtin_bit_cast(uint4, fp8x8_to_bf16(codes.x, codes.y, e8m0_to_f32(sb)));
+        } else {
+          const int d = XStage<NT>::dest(t * cpr + (q >> 1), cpr, m);
+          *reinterpret_cast<uint2*>(xlb + (size_t)d * 16 + 8 * (q & 1)) = codes;
+          if ((q & 3) == 0) xsl[t * kspw + (q >> 2)] = (uint8_t)sb;
+        }
         if (q_out) {
           *reinterpret_cast<uint2*>(q_out + (size_t)t * K + k0 + 8 * q) = codes;
           if ((q & 3) == 0) s_out[(size_t)t * (K >> 5) + (k0 >> 5) + (q >> 2)] = (uint8_t)sb;
@@ -251,12 +301,12 @@ struct XQuant {
 };
 
 // The quantizing rounds past the first (see stage_rest).
-template <int NT>
+template <int NT, bool X16>
 __device__ __attribute__((noinline)) void quant_rest(const uint16_t* xb, int K, size_t k0, int m,
                                                      int cpr8, int xch8, int tid, uint8_t* xlb,
                                                      uint8_t* xsl, uint8_t* q_out,
                                                      uint8_t* s_out) {
-  XQuant<NT> st;
+  XQuant<NT, X16> st;
   for (int c0 = XQuant<NT>::kChunks * NT; c0 < xch8; c0 += XQuant<NT>::kChunks * NT) {
     st.load(xb, K, k0, cpr8, xch8, c0, tid);
     st.store(xlb, xsl, K, k0, m, cpr8, xch8, c0, tid, q_out, s_out);
@@ -266,15 +316,17 @@ __device__ __attribute__((noinline)) void quant_rest(const uint16_t* xb, int K, 
 // The rounds of x staging past the first, for slices larger than one round.
 // Kept out of line: its loads would otherwise make the compiler wait for every
 // W load in flight before the main loop of the common one-round case.
-template <int NT, int XR>
+template <int NT, int XR, bool X16>
 __device__ __attribute__((noinline)) void stage_rest(const uint8_t* x, const uint8_t* xs, int K,
                                                      size_t k0, int m, int cpr, int xch, int wpr,
                                                      int nsw, int tid, uint4* xl, uint32_t* xsw) {
-  XStage<NT, XR> st;
+  XStage<NT, XR, X16> st;
   for (int c0 = XStage<NT, XR>::kChunks * NT; c0 < xch; c0 += XStage<NT, XR>::kChunks * NT) {
     st.load(x, K, k0, m, cpr, xch, c0, tid);
-    st.store(xl);
+    if constexpr (X16) st.load_chunk_scales(xs, K, k0, cpr, xch, c0, tid);
+    st.store(xl, m);
   }
+  if constexpr (X16) return;  // the scales went into the BF16 values
   for (int c0 = XStage<NT, XR>::kWords * NT; c0 < nsw; c0 += XStage<NT, XR>::kWords * NT) {
     st.load_scales(xs, K, k0, wpr, nsw, c0, tid);
     st.store_scales(xsw);
@@ -327,7 +379,7 @@ __global__ void pack_weight_kernel(const uint8_t* w, const uint8_t* ws, int n, i
 // XR: MXFP8 x staged in rounds of 4 * XR chunks per thread (the first round's
 // loads all go out before the W prologue).
 // Without a mailbox (a.state null) the kernel is a plain GEMM into c_out.
-template <int RB, int WN, int WK, int D, int SK, bool QX, int XR = 1>
+template <int RB, int WN, int WK, int D, int SK, bool QX, int XR = 1, bool X16 = false>
 __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     __attribute__((amdgpu_waves_per_eu(2))) gemm_publish_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -391,14 +443,17 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   const int nsw = m * wpr;
   const int cpr8 = KS >> 3;  // 8-value BF16 chunks per x row (quantizing stage)
   const int xch8 = m * cpr8;
-  XStage<NT, XR> xst;
-  XQuant<NT> xqs;
+  XStage<NT, XR, X16> xst;
+  XQuant<NT, X16> xqs;
   if (!ctl) {
     if constexpr (QX) {
       xqs.load(a.xb, K, kslice0, cpr8, xch8, 0, tid);
     } else {
       xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
-      xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
+      if constexpr (X16)
+        xst.load_chunk_scales(a.xs, K, kslice0, cpr, xch, 0, tid);
+      else
+        xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
     }
   }
 
@@ -454,13 +509,14 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
       uint8_t* xlb = reinterpret_cast<uint8_t*>(xl);
       xqs.store(xlb, xsl, K, kslice0, m, cpr8, xch8, 0, tid, qo, so);
       if (xch8 > XQuant<NT>::kChunks * NT)
-        quant_rest<NT>(a.xb, K, kslice0, m, cpr8, xch8, tid, xlb, xsl, qo, so);
+        quant_rest<NT, X16>(a.xb, K, kslice0, m, cpr8, xch8, tid, xlb, xsl, qo, so);
     } else {
       uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
-      xst.store(xl);
-      xst.store_scales(xsw);
-      if (xch > XStage<NT, XR>::kChunks * NT || nsw > XStage<NT, XR>::kWords * NT)
-        stage_rest<NT, XR>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
+      xst.pin_scales();
+      xst.store(xl, m);
+      if constexpr (!X16) xst.store_scales(xsw);
+      if (xch > XStage<NT, XR>::kChunks * NT || (!X16 && nsw > XStage<NT, XR>::kWords * NT))
+        stage_rest<NT, XR, X16>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl, xsw);
     }
   }
   if (S == 1 && tid == hand_tid) {
@@ -507,6 +563,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   for (int i = 0; i < RB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   const bool tok = r16 < m;
   const int xrow = tok ? r16 : 0;  // x row this lane's B operand reads
+  const uint4* xbp = xl + grp * m + xrow;  // X16: this lane's first BF16 piece
   const int kspw = KS >> 5;  // scale bytes per x row in the slice
   const int sb0 = grp >> 1;  // 32-block of this lane's first 16 K (its second is sb0 + 2)
   auto consume = [&](int d, int j) __attribute__((always_inline)) {
@@ -515,7 +572,11 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     // Lanes past the last token convert token 0's values instead: the MFMA
     // columns they feed are never read, and no lane branches.
     v8bf bx[4];
-    {
+    if constexpr (X16) {
+      // Exact BF16 values staged by XStage / XQuant (dest16 layout).
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bx[q] = __builtin_bit_cast(v8bf, xbp[(kb * 16 + q * 4) * m]);
+    } else {
       const uint4 xlo = xl[((kb * 2 + 0) * 4 + grp) * m + xrow];
       const uint4 xhi = xl[((kb * 2 + 1) * 4 + grp) * m + xrow];
       const uint8_t* xsr = xsl + xrow * kspw + kb * 4;
@@ -704,31 +765,50 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
 struct Variant {
   TileCfg cfg;
   int split_k;
-  const void* fn;    // MXFP8 x
-  const void* fn_q;  // BF16 x, quantized in the activation stage
+  const void* fn;      // MXFP8 x
+  const void* fn_q;    // BF16 x, quantized in the activation stage
+  const void* fn16;    // MXFP8 x, staged as BF16 (null: not built)
+  const void* fn16_q;  // BF16 x, quantized and staged as BF16 (null: not built)
 };
 
+#define MXG_FN(RB, WN, WK, D, SK, QX, XR, X16) \
+  reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, QX, XR, X16>)
 #define MXG_V(RB, WN, WK, D, SK)                                                     \
-  Variant{TileCfg{RB, WN, WK, D}, SK,                                                \
-          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, false>), \
-          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, true>)}
+  Variant{TileCfg{RB, WN, WK, D}, SK, MXG_FN(RB, WN, WK, D, SK, false, 1, false),    \
+          MXG_FN(RB, WN, WK, D, SK, true, 1, false), nullptr, nullptr}
+// Also built with x staged as BF16 (the tiles the chooser takes for the
+// workload shapes).
+#define MXG_V16(RB, WN, WK, D, SK)                                                   \
+  Variant{TileCfg{RB, WN, WK, D}, SK, MXG_FN(RB, WN, WK, D, SK, false, 1, false),    \
+          MXG_FN(RB, WN, WK, D, SK, true, 1, false),                                 \
+          MXG_FN(RB, WN, WK, D, SK, false, 1, true), MXG_FN(RB, WN, WK, D, SK, true, 1, true)}
 // The two-round x stage (xr = 2); BF16 x stages through XQuant either way.
-#define MXG_V2(RB, WN, WK, D, SK)                                                        \
-  Variant{TileCfg{RB, WN, WK, D, 2}, SK,                                                 \
-          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, false, 2>), \
-          reinterpret_cast<const void*>(&gemm_publish_kernel<RB, WN, WK, D, SK, true>)}
+// Not built with x staged as BF16: on C3's m = 8, split-K 4 shape that was
+// 1 us slower.
+#define MXG_V2(RB, WN, WK, D, SK)                                                    \
+  Variant{TileCfg{RB, WN, WK, D, 2}, SK, MXG_FN(RB, WN, WK, D, SK, false, 2, false), \
+          MXG_FN(RB, WN, WK, D, SK, true, 1, false), nullptr, nullptr}
 #define MXG_VARIANT(RB, WN, WK, D) \
   MXG_V(RB, WN, WK, D, 1), MXG_V(RB, WN, WK, D, 2), MXG_V(RB, WN, WK, D, 4), \
       MXG_V(RB, WN, WK, D, 8)
+#define MXG_VARIANT16(RB, WN, WK, D) \
+  MXG_V16(RB, WN, WK, D, 1), MXG_V16(RB, WN, WK, D, 2), MXG_V16(RB, WN, WK, D, 4), \
+      MXG_V16(RB, WN, WK, D, 8)
 
 const Variant kVariants[] = {
-    MXG_VARIANT(1, 1, 4, 4), MXG_VARIANT(1, 1, 8, 4), MXG_V(1, 1, 16, 4, 1),
-    MXG_VARIANT(1, 4, 1, 8), MXG_VARIANT(1, 4, 1, 3), MXG_VARIANT(1, 7, 1, 8),
-    MXG_VARIANT(1, 7, 1, 4), MXG_VARIANT(1, 7, 1, 3), MXG_VARIANT(1, 2, 2, 8),
+    MXG_VARIANT16(1, 1, 4, 4), MXG_VARIANT(1, 1, 8, 4), MXG_V16(1, 1, 16, 4, 1),
+    MXG_VARIANT(1, 4, 1, 8), MXG_VARIANT16(1, 4, 1, 3), MXG_VARIANT(1, 7, 1, 8),
+    MXG_VARIANT(1, 7, 1, 4), MXG_VARIANT16(1, 7, 1, 3), MXG_VARIANT16(1, 2, 2, 8),
     MXG_VARIANT(1, 4, 2, 8), MXG_VARIANT(2, 1, 4, 4), MXG_VARIANT(1, 8, 1, 8),
     MXG_VARIANT(2, 2, 2, 4),
     MXG_V2(1, 4, 1, 3, 1), MXG_V2(1, 4, 1, 3, 2), MXG_V2(1, 4, 1, 3, 4), MXG_V2(1, 4, 1, 3, 8),
 };
+
+// The kernel of a variant for an activation form and x staging (null: the
+// variant is not built with that staging).
+const void* variant_fn(const Variant& v, bool bf16_x, bool x16) {
+  return x16 ? (bf16_x ? v.fn16_q : v.fn16) : (bf16_x ? v.fn_q : v.fn);
+}
 
 const Variant* find_variant(const TileCfg& c, int split_k) {
   for (const Variant& v : kVariants)
@@ -742,7 +822,8 @@ const Variant* find_variant(const TileCfg& c, int split_k) {
 }  // namespace
 
 size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice) {
-  const size_t xbytes = (size_t)m * k_slice + (size_t)m * (k_slice / 32);
+  const size_t xbytes =
+      c.x16 ? 2 * (size_t)m * k_slice : (size_t)m * k_slice + (size_t)m * (k_slice / 32);
   const size_t red = (size_t)c.wk * m * tile_rows(c) * sizeof(float);
   return kHeaderBytes + std::max(xbytes, red);
 }
@@ -753,7 +834,8 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out)
 
 // The choice depends only on the sizes and the device: remembered per key.
 bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
-  if (std::getenv("MXG_TILE")) return choose_tile_uncached(m, n, k, split_k, out);
+  if (std::getenv("MXG_TILE") || std::getenv("MXG_X16"))
+    return choose_tile_uncached(m, n, k, split_k, out);
   static std::mutex mu;
   static std::map<std::tuple<int, int, int, int, int>, std::pair<bool, TileCfg>> cache;
   int dev = 0;
@@ -778,7 +860,8 @@ bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
 static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out) {
   const int ks = k / split_k;
   auto fits = [&](const TileCfg& c) {
-    if (!find_variant(c, split_k) || gemm_lds_bytes(c, m, ks) > 160 * 1024) return false;
+    const Variant* v = find_variant(c, split_k);
+    if (!v || (c.x16 && !v->fn16) || gemm_lds_bytes(c, m, ks) > 160 * 1024) return false;
     if (split_k == 1) return true;
     // The workgroups of one tile wait for each other: the grid must be
     // resident all at once.
@@ -786,13 +869,38 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out)
     const long resident = gemm_resident_blocks(c, split_k, gemm_lds_bytes(c, m, ks));
     return resident > 0 && tiles * split_k <= resident && tiles * split_k <= MXG_WS_MAX_GROUPS;
   };
+  int cus = 256;
+  {
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess)
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (cus < 1) cus = 1;
+  }
+  // x staged as BF16 when the variant has it, it fits (with split-K: and the
+  // grid stays resident), and each CU runs at most one workgroup: measured
+  // 0.3-0.6 us faster on N=7168/K=2048/m=4, N=2048/K=8192/m=8/S=4 and
+  // N=256/K=512/m=1 and on BF16 x, neutral on N=7168/K=8192/m=8/S=4, and
+  // 3-4 us slower on N=4096/K=16384/S=8, where two workgroups share a CU.
+  // MXG_X16=0 keeps the FP8 stage.
+  auto upgrade_x16 = [&](TileCfg& c) {
+    const char* e = std::getenv("MXG_X16");
+    if (e && e[0] == '0') return;
+    const long grid = (long)((n + tile_rows(c) - 1) / tile_rows(c)) * split_k;
+    if (grid > cus) return;
+    TileCfg c2 = c;
+    c2.x16 = 1;
+    if (fits(c2)) c = c2;
+  };
   if (const char* env = std::getenv("MXG_TILE")) {
-    // Measurement override: exactly this variant ("rb,wn,wk,depth[,xr]"), or
-    // no launch at all.
+    // Measurement override: exactly this variant ("rb,wn,wk,depth[,xr[,x16]]",
+    // x16 chosen as usual when not given), or no launch at all.
     TileCfg c{};
-    const int got = std::sscanf(env, "%d,%d,%d,%d,%d", &c.rb, &c.wn, &c.wk, &c.depth, &c.xr);
+    const int got =
+        std::sscanf(env, "%d,%d,%d,%d,%d,%d", &c.rb, &c.wn, &c.wk, &c.depth, &c.xr, &c.x16);
     if (got == 4) c.xr = 1;
-    if ((got != 4 && got != 5) || !fits(c)) return false;
+    if (got < 6) c.x16 = 0;
+    if (got < 4 || (c.x16 != 0 && c.x16 != 1) || !fits(c)) return false;
+    if (got < 6) upgrade_x16(c);
     *out = c;
     return true;
   }
@@ -810,13 +918,6 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out)
   const TileCfg* list = split_k > 1 ? kSplit : kNoSplit;
   const size_t count = split_k > 1 ? sizeof(kSplit) / sizeof(kSplit[0])
                                    : sizeof(kNoSplit) / sizeof(kNoSplit[0]);
-  int cus = 256;
-  {
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess)
-      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (cus < 1) cus = 1;
-  }
   constexpr double kGroupCost = 32768.0;  // bytes-equivalent fixed cost per workgroup
   bool found = false;
   double best = 0.0;
@@ -840,6 +941,7 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out)
     TileCfg c2 = *out;
     c2.xr = 2;
     if (chunks > 4L * 64 * out->wn * out->wk && fits(c2)) *out = c2;
+    upgrade_x16(*out);
   }
   return found;
 }
@@ -849,8 +951,9 @@ long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes) {
   static std::map<std::tuple<int, int, int, int, int, size_t>, long> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  const auto key =
-      std::make_tuple(dev, c.rb, c.wn, c.wk * 100 + c.depth + 10000 * c.xr, split_k, lds_bytes);
+  const auto key = std::make_tuple(dev, c.rb, c.wn,
+                                   c.wk * 100 + c.depth + 10000 * c.xr + 100000 * c.x16, split_k,
+                                   lds_bytes);
   {
     std::lock_guard<std::mutex> g(mu);
     auto it = cache.find(key);
@@ -860,8 +963,9 @@ long gemm_resident_blocks(const TileCfg& c, int split_k, size_t lds_bytes) {
   if (!v) return -1;
   // Both activation forms of the variant: a shape gets one tile either way.
   int per_cu = 1 << 30, cus = 0;
-  for (const void* fn : {v->fn, v->fn_q}) {
+  for (const void* fn : {variant_fn(*v, false, c.x16), variant_fn(*v, true, c.x16)}) {
     int n = 0;
+    if (!fn) return -1;
     if (lds_bytes > 64 * 1024 &&
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes) !=
             hipSuccess)
@@ -897,7 +1001,8 @@ hipError_t launch_gemm_publish(const GemmArgs& a, const TileCfg& c, hipStream_t 
   const size_t lds = gemm_lds_bytes(c, a.m, a.k / a.split_k);
   GemmArgs args = a;
   args.xcd_groups = a.split_k > 1 && tiles % 8 == 0 ? 1 : 0;
-  const void* fn = a.xb ? v->fn_q : v->fn;
+  const void* fn = variant_fn(*v, a.xb != nullptr, c.x16);
+  if (!fn) return hipErrorInvalidValue;
   if (lds > 64 * 1024) {
     const hipError_t e =
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

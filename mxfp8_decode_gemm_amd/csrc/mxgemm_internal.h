@@ -34,9 +34,14 @@ struct GemmArgs {
 // K slice; its 64 * wn * wk threads form wn x wk waves (wn along rows, wk
 // along K); each wave keeps `depth` K-blocks of W loads in flight.
 // xr: rounds of 4 chunks per thread in the activation stage's first round.
+// x16: the activation stage converts the x slice to its exact BF16 values on
+// the way into LDS (B operand order), so the main loop reads the B operand
+// without converting it; taken when the variant is built with it and its
+// 2 m k_slice bytes of LDS fit.
 struct TileCfg {
   int rb, wn, wk, depth;
   int xr = 1;
+  int x16 = 0;
 };
 
 inline int tile_rows(const TileCfg& c) { return 16 * c.rb * c.wn; }
@@ -45,11 +50,13 @@ inline int tile_threads(const TileCfg& c, int split_k) {
   return 64 * (c.wn * c.wk + (split_k > 1 ? 1 : 0));
 }
 
-// Dynamic LDS bytes of a launch (x slice, its scales, the partial tile).
+// Dynamic LDS bytes of a launch (x slice and its scales, or its BF16 form when
+// c.x16; the partial tile).
 size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice);
 
-// The tile for a problem; MXG_TILE="rb,wn,wk,depth[,xr]" forces one variant (and
-// fails when it does not fit). Returns false when no variant fits.
+// The tile for a problem; MXG_TILE="rb,wn,wk,depth[,xr[,x16]]" forces one
+// variant (and fails when it does not fit), MXG_X16=0 keeps x in FP8 in LDS.
+// Returns false when no variant fits.
 bool choose_tile(int m, int n, int k, int split_k, TileCfg* out);
 
 // Whether a variant is compiled in.

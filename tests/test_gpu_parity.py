@@ -121,10 +121,18 @@ def test_rows_and_ragged_n(env, m):
 
 
 # Every kernel variant of the library (rows-per-wave blocks, waves along
-# rows, waves along K, load depth), forced through the MXG_TILE override.
+# rows, waves along K, load depth), forced through the MXG_TILE override. The
+# fifth field is the first staging round's size, the sixth whether x is also
+# kept as BF16 in LDS (without it: BF16 when it fits, the default).
 TILES = ["1,1,4,4", "1,1,8,4", "1,1,16,4", "1,4,1,8", "1,4,1,3", "1,7,1,8", "1,7,1,4",
          "1,7,1,3", "1,2,2,8", "1,4,2,8", "2,1,4,4", "1,8,1,8", "2,2,2,4",
-         "1,4,1,3,2"]  # the last: two-round activation stage
+         "1,4,1,3,2",  # two-round activation stage
+         # x left in FP8 in LDS, converted by every wave
+         "1,1,4,4,1,0", "1,1,16,4,1,0", "1,4,1,3,1,0", "1,7,1,3,1,0", "1,2,2,8,1,0",
+         "1,4,1,3,2,0",
+         # x staged as BF16 forced (refused where it does not fit), also at
+         # splits the chooser keeps in FP8
+         "1,7,1,3,1,1", "1,4,1,3,1,1"]
 
 
 @pytest.mark.parametrize("tile", TILES)
@@ -147,14 +155,18 @@ def test_every_tile_variant(env, tile, monkeypatch):
                 ran += 1
             except mx.MxgUnsupported:
                 _say(f"tile {tile} unsupported at m={m} k={k} split_k={s}")
-    assert ran >= (4 if tile == "1,1,16,4" else 8)
+    assert ran >= (4 if tile.startswith("1,1,16,4") else 8)
 
 
-def test_single_nonzero_sweep(env):
+@pytest.mark.parametrize("x16,split", [("auto", 1), ("0", 1), ("auto", 4), ("0", 4)])
+def test_single_nonzero_sweep(env, x16, split, monkeypatch):
     """One nonzero W element and one nonzero x element at swept positions: the
     result is one exact product, so any slip of the MFMA lane, K-piece or
-    scale mapping shows up bit for bit."""
+    scale mapping shows up bit for bit. With x kept as BF16 in LDS (the
+    default where it fits) and in FP8 (MXG_X16=0), with and without split-K."""
     mx, dv = env
+    if x16 == "0":
+        monkeypatch.setenv("MXG_X16", "0")
     codecs, gemm, _, _ = _oracle()
     from workloads.generate import Problem
 
@@ -164,6 +176,7 @@ def test_single_nonzero_sweep(env):
                                                                    127, 128, 200, 511)
                  for t in (0, 3, 7)]
     mbx = dv.Mailbox(1, 2 * m * n)
+    wsp = dv.Workspace(n, split) if split > 1 else None
     c_out = torch.empty(m * n, dtype=torch.int16, device="cuda")
     for (r, kk, t) in positions:
         w = np.zeros((n, k), np.uint8)
@@ -177,8 +190,8 @@ def test_single_nonzero_sweep(env):
         # background scales of other blocks must not leak in
         ws[r, (kk // 32 + 1) % (k // 32)] = 140
         xs[t, (kk // 32 + 2) % (k // 32)] = 100
-        p = Problem("single", m, n, k, 1, w, ws, x, xs, 0)
-        dv.publish(mbx, dv.Operands(p), 1, None, c_out)
+        p = Problem("single", m, n, k, split, w, ws, x, xs, 0)
+        dv.publish(mbx, dv.Operands(p), split, wsp, c_out)
         out = dv.collect(mbx, p.out_bytes)
         torch.cuda.synchronize()
         got = dv.as_u16(out).reshape(m, n)
