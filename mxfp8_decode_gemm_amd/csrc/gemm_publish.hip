@@ -136,6 +136,8 @@ __device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
 // the MFMA B operand reads them: chunk (kb, half, group, t) holds
 // x[t][kb*128 + 64*half + 16*group .. +16).
 // XR scales the round: 4 * XR chunks per thread, all loaded up front.
+// X16: each chunk is stored as its sixteen exact BF16 values instead (two
+// 16-byte pieces, dest16), converted with the scale byte loaded beside it.
 template <int NT, int XR = 1, bool X16 = false>
 struct XStage {
   static constexpr int kChunks = 4 * XR;  // chunks per thread per round
@@ -247,7 +249,8 @@ struct XStage {
 // chunks of a round all lie past the slice skips them (loads and
 // arithmetic); the test is on the wave's first chunk, so it is uniform. With
 // q_out the codes and scales also go to [m, K] and [m, K/32] in global
-// memory.
+// memory. X16: LDS gets the codes' exact BF16 values (XStage::dest16 pieces)
+// instead of codes and scales.
 template <int NT, bool X16 = false>
 struct XQuant {
   static constexpr int kChunks = 8;  // chunks per thread per round
@@ -378,6 +381,8 @@ __global__ void pack_weight_kernel(const uint8_t* w, const uint8_t* ws, int n, i
 // QX: x arrives as BF16 (a.xb) and is quantized in the activation stage.
 // XR: MXFP8 x staged in rounds of 4 * XR chunks per thread (the first round's
 // loads all go out before the W prologue).
+// X16: the staged slice holds exact BF16 values (XStage::dest16 layout), not
+// FP8 codes and scale bytes, and the main loop reads the B operand as is.
 // Without a mailbox (a.state null) the kernel is a plain GEMM into c_out.
 template <int RB, int WN, int WK, int D, int SK, bool QX, int XR = 1, bool X16 = false>
 __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
