@@ -804,6 +804,7 @@ const Variant kVariants[] = {
     MXG_VARIANT16(1, 1, 4, 4), MXG_VARIANT(1, 1, 8, 4), MXG_V16(1, 1, 16, 4, 1),
     MXG_VARIANT(1, 4, 1, 8), MXG_VARIANT16(1, 4, 1, 3), MXG_VARIANT(1, 7, 1, 8),
     MXG_VARIANT(1, 7, 1, 4), MXG_VARIANT16(1, 7, 1, 3), MXG_VARIANT16(1, 2, 2, 8),
+    MXG_VARIANT16(1, 7, 1, 5), MXG_VARIANT16(1, 2, 2, 5),
     MXG_VARIANT(1, 4, 2, 8), MXG_VARIANT(2, 1, 4, 4), MXG_VARIANT(1, 8, 1, 8),
     MXG_VARIANT(2, 2, 2, 4),
     MXG_V2(1, 4, 1, 3, 1), MXG_V2(1, 4, 1, 3, 2), MXG_V2(1, 4, 1, 3, 4), MXG_V2(1, 4, 1, 3, 8),
@@ -916,9 +917,14 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out)
   // whole chip's loads are queued at once. Fitted to sweeps of every variant
   // on N=7168/K=8192/m=8/S=4, N=7168/K=2048/m=4, N=4096/K=16384 (m 1..8,
   // S 1/4/8), N=7168/K=4096/m=1/S=4 and N=2048/K=8192/m=8/S=4.
-  static const TileCfg kSplit[] = {{1, 7, 1, 3}, {1, 4, 1, 3}, {1, 2, 2, 8}, {1, 7, 1, 4},
-                                   {1, 4, 1, 8}, {1, 4, 2, 8}, {2, 1, 4, 4}, {1, 1, 4, 4}};
-  static const TileCfg kNoSplit[] = {{1, 1, 16, 4}, {1, 1, 8, 4}, {1, 2, 2, 8},
+  // After the B operand stopped being converted in every wave, deeper rings
+  // paid on the 112- and 32-row tiles (depth 5: N=7168/K=8192/m=8/S=4 14.3 ->
+  // 13.95 us, N=7168/K=2048/m=4 6.5 -> 6.1 us, N=2048/K=8192/m=8/S=4 8.5 ->
+  // 8.2 us) and not on the 64-row one.
+  static const TileCfg kSplit[] = {{1, 7, 1, 5}, {1, 4, 1, 3}, {1, 2, 2, 5}, {1, 7, 1, 3},
+                                   {1, 2, 2, 8}, {1, 7, 1, 4}, {1, 4, 1, 8}, {1, 4, 2, 8},
+                                   {2, 1, 4, 4}, {1, 1, 4, 4}};
+  static const TileCfg kNoSplit[] = {{1, 1, 16, 4}, {1, 1, 8, 4}, {1, 2, 2, 5}, {1, 2, 2, 8},
                                      {1, 4, 1, 3}, {1, 1, 4, 4}, {2, 1, 4, 4}};
   const TileCfg* list = split_k > 1 ? kSplit : kNoSplit;
   const size_t count = split_k > 1 ? sizeof(kSplit) / sizeof(kSplit[0])

@@ -125,14 +125,14 @@ def test_rows_and_ragged_n(env, m):
 # fifth field is the first staging round's size, the sixth whether x is also
 # kept as BF16 in LDS (without it: BF16 when it fits, the default).
 TILES = ["1,1,4,4", "1,1,8,4", "1,1,16,4", "1,4,1,8", "1,4,1,3", "1,7,1,8", "1,7,1,4",
-         "1,7,1,3", "1,2,2,8", "1,4,2,8", "2,1,4,4", "1,8,1,8", "2,2,2,4",
+         "1,7,1,3", "1,7,1,5", "1,2,2,8", "1,2,2,5", "1,4,2,8", "2,1,4,4", "1,8,1,8", "2,2,2,4",
          "1,4,1,3,2",  # two-round activation stage
          # x left in FP8 in LDS, converted by every wave
          "1,1,4,4,1,0", "1,1,16,4,1,0", "1,4,1,3,1,0", "1,7,1,3,1,0", "1,2,2,8,1,0",
          "1,4,1,3,2,0",
          # x staged as BF16 forced (refused where it does not fit), also at
          # splits the chooser keeps in FP8
-         "1,7,1,3,1,1", "1,4,1,3,1,1"]
+         "1,7,1,3,1,1", "1,4,1,3,1,1", "1,7,1,5,1,0", "1,2,2,5,1,0"]
 
 
 @pytest.mark.parametrize("tile", TILES)
