@@ -184,7 +184,16 @@ int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int3
  * PublishingMxfp8Linear.precompile: a publish without its consumer would
  * desynchronize the mailbox). Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY
  * (2mn > capacity), MXG_EWORKSPACE, MXG_EUNSUPPORTED (the split-K grid cannot
- * be co-resident on this device), MXG_EHIP. */
+ * be co-resident on this device), MXG_EHIP.
+ *
+ * The kernel variant (rows per workgroup, waves, W ring depth, whether x is
+ * staged in LDS as BF16) is chosen from m, n, k, split_k and the device. Ring
+ * depth and x staging leave the result bits unchanged; the number of waves
+ * along K sets the FP32 summation order, so variants that differ there agree
+ * to rounding, not bit for bit. For measurement and tests the environment
+ * variable MXG_TILE="rb,wn,wk,depth[,xr[,x16]]" forces one variant
+ * (MXG_EUNSUPPORTED when it is not built or does not fit), and MXG_X16=0
+ * keeps x staged as FP8. */
 int mxgemm_publish(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
                    const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n,
                    int32_t k, int32_t split_k, void* workspace,
