@@ -102,6 +102,8 @@ def _fused_case(env, p, xbits, split_k, ranks=1):
 @pytest.mark.parametrize("m,n,k,split_k,dist", [
     (8, 1000, 1024, 1, "normal"), (1, 512, 2048, 4, "outliers"), (5, 2056, 4096, 4, "outliers"),
     (8, 1024, 8192, 8, "normal"), (3, 7168, 2048, 2, "outliers"), (8, 7168, 8192, 4, "outliers"),
+    # a K slice that takes more than one quantizing round, staged as BF16
+    (8, 7168, 16384, 4, "outliers"),
 ])
 def test_fused_quantizer_gemm(env, m, n, k, split_k, dist):
     mx, dv = env
