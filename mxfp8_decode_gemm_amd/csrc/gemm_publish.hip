@@ -45,9 +45,9 @@
 //   * Split-K across workgroups: in every token row of a tile, slice s owns
 //     the contiguous pack columns [ceil(s P / S), ceil((s + 1) P / S)) (P packs
 //     per row). The other slices store their partials of those columns as
-//     (FP32 bits, epoch) 64-bit pairs with agent-scope stores; the owner's
-//     poll waves, which have no store of their own in flight, poll all of a
-//     column's pairs in one batch until every tag equals this launch's epoch
+//     (FP32 bits, epoch) 64-bit pairs with agent-scope stores, spread over
+//     every worker wave; the owner's poll waves poll all of a column's pairs
+//     in one batch until every tag equals this launch's epoch
 //     (sync page = vllm.models.deepseek_v41.amd.mono.common.sync, Mailbox: one
 //     round trip, no drain, no flag), then sum the slices in ascending K order.
 //   * One lane per owned column rounds its sum to BF16; lane shuffles gather
@@ -629,12 +629,13 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   // Each 16-byte pack (8 columns of one token) is reduced by one slice: in
   // every token row of the tile, slice s owns the pack columns
   // jc in [ceil(s * PPR / S), ceil((s + 1) * PPR / S)), a contiguous run.
-  // With split-K the first PW waves handle the owned packs (poll, reduce,
-  // publish), one lane per column, and the other waves send the partials
-  // the other slices own. Loads and stores share one in-order completion
-  // counter per wave, so a polling wave must have no store of its own in
-  // flight: its poll then returns as soon as the peers' pairs are there.
-  // Without split-K every wave publishes.
+  // With split-K every worker wave first sends its share of the partials the
+  // other slices own; then the first PW waves handle the owned packs (poll,
+  // reduce, publish), one lane per column. Loads and stores share one
+  // in-order completion counter per wave, so a polling wave's first poll
+  // also waits for its own sends; spreading the sends over every wave still
+  // ends the send phase sooner than keeping the polling waves out of it
+  // (measured). Without split-K every wave publishes.
   constexpr int NW = NT / 64;
   constexpr int PPR = NTILE / 8;  // packs per token row of the tile
   const int jlo = (slice * PPR + SK - 1) / SK;
@@ -647,7 +648,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     pw = pw < 1 ? 1 : (pw > NW - 1 ? NW - 1 : pw);
   }
   const bool poller = wave < pw;
-  const bool sender = SK > 1 && !ctl && (NW == 1 || wave >= pw);
+  const bool sender = SK > 1 && !ctl;
 
   // ---- partial tile -> LDS [wk][t][row], summed over waves in K order ---
   __syncthreads();  // every wave is done with x in LDS
@@ -676,8 +677,8 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   // pairs[((slice * 8 + t) * (N / 8) + n / 8) * 8 + n % 8]; lanes take
   // consecutive columns of a token row, so a wave writes whole packs.
   if (sender) {
-    const int s0 = NW == 1 ? tid : tid - pw * 64;
-    const int ns = NW == 1 ? NT : NT - pw * 64;
+    const int s0 = tid;
+    const int ns = NT;
     for (int q = s0; q < m * NTILE; q += ns) {
       const int t = q / NTILE;
       const int row = q - t * NTILE;
