@@ -27,7 +27,8 @@
 //     of the kernel's time.
 //   * W never touches LDS: it is re-laid once (mxgemm_pack_weight) into 2 KiB
 //     tiles of 16 rows x 128 K, so that each wave instruction reads 1 KiB of
-//     contiguous HBM straight into VGPRs, `depth` K blocks ahead. Lane l holds
+//     contiguous HBM straight into VGPRs, `depth` K blocks ahead, as a raw
+//     buffer load whose block offset is a scalar (no vector address math). Lane l holds
 //     row l % 16 and K = 16*(l/16) + 0..15 and 64 + 16*(l/16) + 0..15 of the
 //     block; the BF16 MFMA pairs A and B elements by lane group and position
 //     (measured), so the B operand uses the same K split.
@@ -103,6 +104,13 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(uint32_t w0, uint32_t w1, float sc
 }
 
 constexpr int kHeaderBytes = 16;
+
+// Raw buffer descriptors (gfx9 family): the fourth word of a plain byte
+// buffer, an offset no descriptor here reaches (1 GiB; offsets at or past a
+// buffer's size read as zeros), and the cache policy of a streaming load.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kPastBuffer = 0x40000000;
+constexpr int kLoadNontemporal = 2;
 
 __device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -469,31 +477,39 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   const int KBT = K >> 7;                     // K blocks per row block
   const int rbn = (N + 15) >> 4;              // packed row blocks
   const int kb0 = slice * NB + kb_lo;         // first absolute K block of this wave
-  const uint8_t* wtile[RB];
-  const uint32_t* stile[RB];
+  // Each of the wave's row blocks is read as a raw buffer over its nbw
+  // contiguous tiles (scales: 64 bytes per tile), so the block offset goes
+  // in a scalar register and the lane's offset stays fixed: no per-load
+  // vector address arithmetic. Rows past N load the last row block (never
+  // published).
+  __amdgpu_buffer_rsrc_t wrs[RB], srs[RB];
 #pragma unroll
   for (int i = 0; i < RB; ++i) {
     int rb = (row0 >> 4) + wn * RB + i;
-    rb = rb < rbn ? rb : rbn - 1;  // row blocks past N load the last one; never published
-    wtile[i] = a.w + ((size_t)rb * KBT + kb0) * 2048 + 16 * lane;
-    stile[i] = reinterpret_cast<const uint32_t*>(a.ws) + ((size_t)rb * KBT + kb0) * 16 + r16;
+    rb = rb < rbn ? rb : rbn - 1;
+    const size_t t0 = (size_t)rb * KBT + kb0;
+    wrs[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.w + t0 * 2048), (short)0, nbw * 2048,
+                                               kBufferWord3);
+    srs[i] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ws + t0 * 64), (short)0, nbw * 64,
+                                               kBufferWord3);
   }
   v4u wlo[D][RB], whi[D][RB];
   uint32_t wsc[D][RB];
-  // Block j of this wave, or (j < 0) an in-bounds dummy: the first 128 bytes
-  // of x and the first scale word of xs (of BF16 x when quantizing), which
-  // every workgroup reads anyway. Every refill slot issues its loads either
-  // way, so the count of loads in flight is the same on every path.
-  const uint8_t* xd = QX ? reinterpret_cast<const uint8_t*>(a.xb) : a.x;
-  const uint32_t* xsd = reinterpret_cast<const uint32_t*>(QX ? xd : a.xs);
+  // Block j of this wave (lane l's pieces at 16 l and 1024 + 16 l, its
+  // scale word at 4 (l % 16)), or (j < 0) a dummy whose offset lies past the
+  // buffer: the hardware returns zeros without a memory access. Every refill
+  // slot issues its loads either way, so the count of loads in flight is the
+  // same on every path.
   auto load_w = [&](int d, int j) __attribute__((always_inline)) {
+    const int vo = j >= 0 ? 16 * lane : kPastBuffer;
+    const int so = j >= 0 ? 4 * r16 : kPastBuffer;
+    const int jo = j >= 0 ? j : 0;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const uint8_t* t = j >= 0 ? wtile[i] + (size_t)j * 2048 : xd + 16 * (lane & 7);
-      const uint32_t* sc = j >= 0 ? stile[i] + (size_t)j * 16 : xsd;
-      wlo[d][i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(t));
-      whi[d][i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(t + (j >= 0 ? 1024 : 0)));
-      wsc[d][i] = *sc;
+      wlo[d][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs[i], vo, jo * 2048, kLoadNontemporal);
+      whi[d][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs[i], vo + 1024, jo * 2048,
+                                                         kLoadNontemporal);
+      wsc[d][i] = __builtin_amdgcn_raw_buffer_load_b32(srs[i], so, jo * 64, 0);
     }
   };
   constexpr int G = D > 16 ? D : 16;  // K blocks per straight-line group
@@ -802,7 +818,9 @@ struct Variant {
       MXG_V16(RB, WN, WK, D, 8)
 
 const Variant kVariants[] = {
-    MXG_VARIANT16(1, 1, 4, 4), MXG_VARIANT(1, 1, 8, 4), MXG_V16(1, 1, 16, 4, 1),
+    // The 16-wave tile keeps the FP8 stage: its BF16 form needs more than the
+    // 128 VGPRs four waves per SIMD allow and spills.
+    MXG_VARIANT16(1, 1, 4, 4), MXG_VARIANT(1, 1, 8, 4), MXG_V(1, 1, 16, 4, 1),
     MXG_VARIANT(1, 4, 1, 8), MXG_VARIANT16(1, 4, 1, 3), MXG_VARIANT(1, 7, 1, 8),
     MXG_VARIANT(1, 7, 1, 4), MXG_VARIANT16(1, 7, 1, 3), MXG_VARIANT16(1, 2, 2, 8),
     MXG_VARIANT16(1, 7, 1, 5), MXG_VARIANT16(1, 2, 2, 5),
