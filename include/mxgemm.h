@@ -209,6 +209,28 @@ int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t*
                          int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
                          uint16_t* c_out, void* stream, void* ev_start, void* ev_stop);
 
+/* mxgemm_publish for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, effects and errors as mxgemm_publish, without the
+ * workspace: with split_k > 1 the (value, tag) pairs and epoch words live in
+ * a library-held device array, one per GPU, held until the process ends,
+ * whose pair region is MXG_NOALLOC_PAIR_BYTES (4 MiB); shapes whose
+ * mxgemm_workspace_bytes exceed MXG_WS_HEADER_BYTES + MXG_WS_FLAG_BYTES +
+ * MXG_NOALLOC_PAIR_BYTES (split_k * ceil(n/8)*8 > 65536) are rejected with
+ * MXG_EWORKSPACE before anything is enqueued. The call allocates nothing and
+ * the array needs no arming: it starts zero-filled, which the kernel reads
+ * as an armed workspace. Every call on a GPU shares that GPU's array and
+ * leaves its contents for the next call, so calls that overlap on one GPU (on
+ * different streams, or with a mxgemm_publish_noalloc of another mailbox in
+ * flight) race and must not be issued; one stream in order is the contract.
+ * A split-K poll that gives up sets MXG_ERR_SPLITK_SPIN in the array's own
+ * header, which no caller can read or clear. split_k == 1 uses no array and
+ * is mxgemm_publish itself. */
+#define MXG_NOALLOC_PAIR_BYTES (4u << 20)
+int mxgemm_publish_noalloc(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                           const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n,
+                           int32_t k, int32_t split_k, uint16_t* c_out, void* stream);
+
 /* mxgemm_publish with the activation in BF16, quantized inside the GEMM
  * (the MXFP8 activation the publishing_gemm page's PublishingMxfp8Linear
  * takes is a QuantizedActivation whose original dtype is BF16; the quantizer

@@ -36,6 +36,7 @@ STATE_PEER_GEN, STATE_PEER_ARR = 8, 16
 WS_HEADER_BYTES = 256
 WS_FLAG_BYTES = 8192
 WS_MAX_GROUPS = 2048
+NOALLOC_PAIR_BYTES = 4 << 20
 WS_EPOCH, WS_ERROR = 0, 2
 ERR_COLLECT_SPIN = 0x1
 ERR_SPLITK_SPIN = 0x2
@@ -93,6 +94,8 @@ def _load() -> ctypes.CDLL:
                                           vp, vp]),
         "mxgemm_publish_timed": (ctypes.c_int, [mbp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
                                                 sz, vp, vp, vp, vp]),
+        "mxgemm_publish_noalloc": (ctypes.c_int, [mbp, vp, vp, vp, vp, i32, i32, i32, i32, vp,
+                                                  vp]),
         "mailbox_publish": (ctypes.c_int, [mbp, i32, vp, i64, vp]),
         "mailbox_collect": (ctypes.c_int, [mbp, vp, i64, vp]),
         "mailbox_collect_sum": (ctypes.c_int, [mbp, vp, i64, vp]),
@@ -238,6 +241,14 @@ def mxgemm_publish_timed(mb: mxg_mailbox, w, w_scale, x, x_scale, m: int, n: int
                                      workspace_bytes, _ptr(c_out), _stream(stream),
                                      _event(ev_start), _event(ev_stop)),
            "mxgemm_publish_timed")
+
+
+def mxgemm_publish_noalloc(mb: mxg_mailbox, w, w_scale, x, x_scale, m: int, n: int, k: int,
+                           split_k: int = 1, c_out=None, stream=None) -> None:
+    _check(_lib.mxgemm_publish_noalloc(ctypes.byref(mb), _ptr(w), _ptr(w_scale), _ptr(x),
+                                       _ptr(x_scale), m, n, k, split_k, _ptr(c_out),
+                                       _stream(stream)),
+           "mxgemm_publish_noalloc")
 
 
 def mailbox_publish(mb: mxg_mailbox, rank: int, src, nbytes: int, stream=None) -> None:

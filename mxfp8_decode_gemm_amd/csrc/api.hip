@@ -96,15 +96,13 @@ int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
                                         static_cast<hipStream_t>(stream)));
 }
 
-namespace {
-// One GEMM launch. mb null: plain GEMM into c_out (required). xb non-null:
-// BF16 x quantized in the kernel (x and x_scale must be null), with the
-// quantized activation optionally written to xq_out / xs_out.
-int gemm_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
-              const uint8_t* x, const uint8_t* x_scale, const uint16_t* xb, int32_t m, int32_t n,
-              int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
-              uint16_t* c_out, uint8_t* xq_out, uint8_t* xs_out, void* stream, void* ev_start,
-              void* ev_stop) {
+}  // extern "C"
+
+namespace mxg {
+int gemm_validate(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                  const uint8_t* x, const uint8_t* x_scale, const uint16_t* xb, int32_t m,
+                  int32_t n, int32_t k, int32_t split_k, uint16_t* c_out, uint8_t* xq_out,
+                  uint8_t* xs_out) {
   if (mb ? !mailbox_ok(mb) : !c_out) return MXG_EINVAL;
   if (!w || !w_scale) return MXG_EINVAL;
   if (xb ? (x || x_scale) : (!x || !x_scale || xq_out || xs_out)) return MXG_EINVAL;
@@ -118,6 +116,20 @@ int gemm_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
     return MXG_EALIGN;
   if (mb && (!aligned16(mb->slots) || !aligned16(mb->state))) return MXG_EALIGN;
   if (mb && (int64_t)2 * m * n > mb->capacity_bytes) return MXG_ECAPACITY;
+  return MXG_OK;
+}
+
+// One GEMM launch. mb null: plain GEMM into c_out (required). xb non-null:
+// BF16 x quantized in the kernel (x and x_scale must be null), with the
+// quantized activation optionally written to xq_out / xs_out.
+int gemm_call(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+              const uint8_t* x, const uint8_t* x_scale, const uint16_t* xb, int32_t m, int32_t n,
+              int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
+              uint32_t epoch_bias, uint16_t* c_out, uint8_t* xq_out, uint8_t* xs_out,
+              void* stream, void* ev_start, void* ev_stop) {
+  const int rc =
+      gemm_validate(mb, w, w_scale, x, x_scale, xb, m, n, k, split_k, c_out, xq_out, xs_out);
+  if (rc != MXG_OK) return rc;
   if (split_k > 1) {
     if (!workspace || workspace_bytes < mxgemm_workspace_bytes(m, n, k, split_k))
       return MXG_EWORKSPACE;
@@ -157,19 +169,22 @@ int gemm_impl(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
   a.k = k;
   a.split_k = split_k;
   a.spin_limit = spin_limit();
+  a.epoch_bias = epoch_bias;
   return hip_code(launch_gemm_publish(a, cfg, static_cast<hipStream_t>(stream),
                                       static_cast<hipEvent_t>(ev_start),
                                       static_cast<hipEvent_t>(ev_stop)));
 }
-}  // namespace
+}  // namespace mxg
+
+extern "C" {
 
 int mxgemm_publish(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
                    const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n, int32_t k,
                    int32_t split_k, void* workspace, size_t workspace_bytes, uint16_t* c_out,
                    void* stream) {
   if (!mb) return MXG_EINVAL;
-  return gemm_impl(mb, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
-                   workspace_bytes, c_out, nullptr, nullptr, stream, nullptr, nullptr);
+  return gemm_call(mb, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
+                   workspace_bytes, 0, c_out, nullptr, nullptr, stream, nullptr, nullptr);
 }
 
 int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
@@ -177,8 +192,8 @@ int mxgemm_publish_timed(const mxg_mailbox* mb, const uint8_t* w, const uint8_t*
                          int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
                          uint16_t* c_out, void* stream, void* ev_start, void* ev_stop) {
   if (!mb || !ev_start || !ev_stop) return MXG_EINVAL;
-  return gemm_impl(mb, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
-                   workspace_bytes, c_out, nullptr, nullptr, stream, ev_start, ev_stop);
+  return gemm_call(mb, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
+                   workspace_bytes, 0, c_out, nullptr, nullptr, stream, ev_start, ev_stop);
 }
 
 int mxgemm_publish_bf16(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
@@ -186,16 +201,16 @@ int mxgemm_publish_bf16(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* 
                         void* workspace, size_t workspace_bytes, uint16_t* c_out,
                         uint8_t* x_q_out, uint8_t* x_scale_out, void* stream) {
   if (!mb || !x) return MXG_EINVAL;
-  return gemm_impl(mb, w, w_scale, nullptr, nullptr, x, m, n, k, split_k, workspace,
-                   workspace_bytes, c_out, x_q_out, x_scale_out, stream, nullptr, nullptr);
+  return gemm_call(mb, w, w_scale, nullptr, nullptr, x, m, n, k, split_k, workspace,
+                   workspace_bytes, 0, c_out, x_q_out, x_scale_out, stream, nullptr, nullptr);
 }
 
 int mxgemm(const uint8_t* w, const uint8_t* w_scale, const uint8_t* x, const uint8_t* x_scale,
            int32_t m, int32_t n, int32_t k, int32_t split_k, void* workspace,
            size_t workspace_bytes, uint16_t* c_out, void* stream) {
   if (!c_out) return MXG_EINVAL;
-  return gemm_impl(nullptr, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
-                   workspace_bytes, c_out, nullptr, nullptr, stream, nullptr, nullptr);
+  return gemm_call(nullptr, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
+                   workspace_bytes, 0, c_out, nullptr, nullptr, stream, nullptr, nullptr);
 }
 
 int mxfp8_quantize(const uint16_t* x, int32_t rows, int32_t k, uint8_t* x_q, uint8_t* x_scale,

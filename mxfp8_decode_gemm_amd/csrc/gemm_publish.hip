@@ -446,7 +446,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   uint32_t gen = 0, epoch = 0;
   if (tid == hand_tid) {
     if (a.state) gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
-    if (S > 1) epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH);
+    if (S > 1) epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH) + a.epoch_bias;
   }
 
   // ---- x slice, first round: loads issued before the W stream -----------
@@ -574,7 +574,8 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
         }
         __builtin_amdgcn_s_sleep(2);
       }
-      if (ok && lane == 0) st_agent_u32(a.ws_hdr + MXG_WS_EPOCH, e + 1u == 0u ? 1u : e + 1u);
+      if (ok && lane == 0)
+        st_agent_u32(a.ws_hdr + MXG_WS_EPOCH, (e + 1u == 0u ? 1u : e + 1u) - a.epoch_bias);
     }
   }
 

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/mxgemm.h"
+
 namespace mxg {
 
 // Everything one GEMM+publish launch needs, by value.
@@ -28,6 +30,11 @@ struct GemmArgs {
   int32_t m, n, k, split_k;
   uint32_t spin_limit;
   int32_t xcd_groups; // set by the launcher: the slices of a tile share an XCD
+  // Added to the workspace's stored EPOCH word on every read and taken off
+  // on every write: 0 for a workspace armed by mxgemm_workspace_init (stored
+  // EPOCH starts at 1), 1 for the library's zero-filled no-allocation
+  // scratch (stored 0 means epoch 1). Epoch 0 is never live either way.
+  uint32_t epoch_bias;
 };
 
 // A workgroup computes an output tile of n_tile = 16 * rb * wn rows for one
@@ -102,5 +109,21 @@ hipError_t launch_mailbox_all_gather(uint8_t* slots, int64_t gen_stride, int64_t
                                      hipStream_t s);
 
 uint32_t spin_limit();
+
+// Host validation of a GEMM call from sizes and addresses alone, everything
+// but the workspace: MXG_OK or the code gemm_call would return.
+int gemm_validate(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
+                  const uint8_t* x, const uint8_t* x_scale, const uint16_t* xb, int32_t m,
+                  int32_t n, int32_t k, int32_t split_k, uint16_t* c_out, uint8_t* xq_out,
+                  uint8_t* xs_out);
+
+// One GEMM launch after host validation (the body of mxgemm_publish and its
+// siblings). mb null: plain GEMM into c_out. xb non-null: BF16 x quantized in
+// the kernel. epoch_bias: see GemmArgs. Returns an MXG_* code.
+int gemm_call(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale, const uint8_t* x,
+              const uint8_t* x_scale, const uint16_t* xb, int32_t m, int32_t n, int32_t k,
+              int32_t split_k, void* workspace, size_t workspace_bytes, uint32_t epoch_bias,
+              uint16_t* c_out, uint8_t* xq_out, uint8_t* xs_out, void* stream, void* ev_start,
+              void* ev_stop);
 
 }  // namespace mxg

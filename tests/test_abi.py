@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -144,6 +144,36 @@ def test_misc(mx):
     assert lib.mxgemm_workspace_init(None, 1024, None) == -1
     assert lib.mxgemm_workspace_init(4096, 1024, None) == -1  # below header + epoch words
     assert lib.mxgemm_workspace_init(4100, 8448, None) == -2
+
+
+def test_noalloc_validation(mx):
+    """mxgemm_publish_noalloc: mxgemm_publish's rules, plus a refusal of split-K
+    shapes whose pairs do not fit the library's array (split_k * ceil(n/8)*8 >
+    65536), all decided on the host before any HIP call."""
+    lib = mx.library()
+    mb = _mb(mx, cap=1 << 20)
+
+    def call(**kw):
+        a = dict(w=4096, ws=4096, x=4096, xs=4096, m=1, n=256, k=1024, s=1, c=None)
+        a.update(kw)
+        return lib.mxgemm_publish_noalloc(ctypes.byref(mb), a["w"], a["ws"], a["x"], a["xs"],
+                                          a["m"], a["n"], a["k"], a["s"], a["c"], None)
+
+    assert lib.mxgemm_publish_noalloc(None, 4096, 4096, 4096, 4096, 1, 256, 1024, 1, None,
+                                      None) == -1
+    assert call(m=9) == -1
+    assert call(n=12) == -1
+    assert call(s=3) == -1
+    assert call(s=8, k=512) == -1
+    assert call(w=None) == -1
+    assert call(x=4100) == -2
+    assert call(c=8200) == -2
+    assert call(n=1 << 20) == -3           # 2 m n above the slot
+    assert call(n=16384, s=8) == -4        # 8 * 16384 pairs columns > 65536
+    assert call(n=65536 + 8, s=2) == -4
+    assert mx.NOALLOC_PAIR_BYTES == 4 << 20
+    with open(os.path.join(ROOT, "include", "mxgemm.h")) as f:
+        assert "#define MXG_NOALLOC_PAIR_BYTES (4u << 20)" in f.read()
 
 
 def test_bf16_publish_validation(mx):
