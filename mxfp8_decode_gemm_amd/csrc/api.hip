@@ -74,7 +74,9 @@ size_t mxgemm_packed_weight_bytes(int32_t n, int32_t k) {
 
 size_t mxgemm_packed_scale_bytes(int32_t n, int32_t k) {
   if (n <= 0 || k <= 0 || k % 128) return 0;
-  return (size_t)((n + 15) / 16) * 16 * (size_t)(k / 32);
+  const size_t rbn = (size_t)((n + 15) / 16);
+  // the scale tiles, then one range word per row block (rounded to 16 bytes)
+  return rbn * 16 * (size_t)(k / 32) + (rbn * 4 + 15) / 16 * 16;
 }
 
 int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int32_t k,

@@ -124,7 +124,10 @@ def test_all_gather_overlap(mx):
 def test_pack_sizes_and_validation(mx):
     assert mx.mxgemm_packed_weight_bytes(7168, 8192) == 7168 * 8192
     assert mx.mxgemm_packed_weight_bytes(24, 128) == 32 * 128
-    assert mx.mxgemm_packed_scale_bytes(24, 128) == 32 * 4
+    # scale tiles, then one range word per 16-row block rounded up to 16 bytes
+    assert mx.mxgemm_packed_scale_bytes(24, 128) == 32 * 4 + 16
+    assert mx.mxgemm_packed_scale_bytes(7168, 8192) == 7168 * 256 + 448 * 4
+    assert mx.mxgemm_packed_scale_bytes(80, 128) == 80 * 4 + 32
     assert mx.mxgemm_packed_weight_bytes(8, 96) == 0
     lib = mx.library()
     assert lib.mxgemm_pack_weight(4096, 4096, 12, 128, 4096, 4096, None) == -1

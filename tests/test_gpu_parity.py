@@ -140,22 +140,27 @@ def test_every_tile_variant(env, tile, monkeypatch):
     """Each variant on a ragged N at every split it is built for, with 1, 5
     and 8 tokens and K slices down to one 128-wide block (waves along K left
     without work), and m = 8 at K = 8192, whose activation slice takes several
-    staging rounds. The 16-wave variant has no split-K form (its control wave
-    would pass 1024 threads)."""
+    staging rounds; then with scale bytes at both E8M0 ends, which every
+    workgroup meets and so takes the exact path (x staged as FP8 again where
+    the variant staged it as BF16). The 16-wave variant has no split-K form
+    (its control wave would pass 1024 threads)."""
     mx, _ = env
     from workloads import generate
 
     monkeypatch.setenv("MXG_TILE", tile)
     ran = 0
-    for m, k in [(1, 2048), (5, 1024), (8, 2048), (8, 8192)]:
+    for m, k, extreme in [(1, 2048, False), (5, 1024, False), (8, 2048, False),
+                          (8, 8192, False), (3, 2048, True), (8, 8192, True)]:
         for s in [1, 2, 4, 8]:
             p = generate.random_problem(7000 + 10 * m + s + k, m, 1000, k, s)
+            if extreme:  # scale bytes at both E8M0 ends: the exact path
+                p = generate.extreme_scales(p, 7001 + m + s)
             try:
                 run_case(env, p, split_k=s, calls=2)
                 ran += 1
             except mx.MxgUnsupported:
                 _say(f"tile {tile} unsupported at m={m} k={k} split_k={s}")
-    assert ran >= (4 if tile.startswith("1,1,16,4") else 8)
+    assert ran >= (6 if tile.startswith("1,1,16,4") else 12)
 
 
 @pytest.mark.parametrize("x16,split", [("auto", 1), ("0", 1), ("auto", 4), ("0", 4)])
@@ -220,13 +225,35 @@ def test_closed_forms(env):
     run_case(env, p2)
 
 
-def test_negative_zero_and_zero_rows(env):
+@pytest.mark.parametrize("split_k", [1, 4])
+def test_negative_zero_and_zero_rows(env, split_k):
+    """The stress recipe: zero rows (of +0 and -0 codes) publish 0x0000, and
+    the tiny rows' results, single products below 2^-135 in magnitude, reach
+    the epilogue as BF16 zeros of the product's sign: 0x8000 in the raw output
+    wherever the product is negative, 0x0000 in the mailbox everywhere."""
+    mx, dv = env
+    codecs, gemm, _, _ = _oracle()
     from workloads import generate
 
-    p = generate.random_problem(77, 8, 512, 1024, 4, "stress")
-    own, bits, _ = run_case(env, p, split_k=4)
+    p = generate.random_problem(77, 8, 512, 1024, split_k, "stress")
+    own, bits, _ = run_case(env, p, split_k=split_k)
     zr = np.r_[p.meta["zero_rows_pos"], p.meta["zero_rows_neg"], p.meta["tiny_rows"]]
     assert np.all(own[:, zr] == 0)
+    ops = dv.Operands(p)
+    mbx = dv.Mailbox(1, p.out_bytes)
+    ws = dv.Workspace(p.n, split_k) if split_k > 1 else None
+    c = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
+    dv.publish(mbx, ops, split_k, ws, c)
+    got = dv.as_u16(dv.collect(mbx, p.out_bytes)).reshape(p.m, p.n)
+    torch.cuda.synchronize()
+    raw = dv.as_u16(c).reshape(p.m, p.n)
+    exact, _ = gemm.gemm_f64(p.w, p.ws, p.x, p.xs)
+    tiny = p.meta["tiny_rows"]
+    neg = exact[:, tiny] < 0
+    assert neg.any() and (exact[:, tiny] > 0).any()
+    assert np.all(raw[:, tiny][neg] == 0x8000)
+    assert np.all(raw[:, tiny][~neg] == 0x0000)
+    assert np.all(got[:, tiny] == 0) and np.all(got == codecs.clear_negative_zero(raw))
 
 
 def test_fused_equals_unfused(env):
@@ -409,7 +436,8 @@ def test_pack_weight_layout(env, n, k):
     wp = wp.cpu().numpy()
     wsp = wsp.cpu().numpy()
     rbn, kbt = -(-n // 16), k // 128
-    assert wp.size == rbn * kbt * 2048 and wsp.size == rbn * kbt * 64
+    assert wp.size == rbn * kbt * 2048
+    assert wsp.size == rbn * kbt * 64 + -(-rbn * 4 // 16) * 16
     expect = np.zeros(rbn * kbt * 2048, np.uint8)
     sexp = np.full(rbn * kbt * 64, 127, np.uint8)
     for rb in range(rbn):
@@ -427,7 +455,13 @@ def test_pack_weight_layout(env, n, k):
                 if row < n:
                     sexp[(t * 16 + r) * 4:(t * 16 + r) * 4 + 4] = ws[row, kb * 4:kb * 4 + 4]
     assert np.array_equal(wp, expect)
-    assert np.array_equal(wsp, sexp)
+    assert np.array_equal(wsp[: sexp.size], sexp)
+    # one range word per row block: smallest and largest scale byte of its
+    # rows (rows past n count as 127)
+    words = wsp[sexp.size: sexp.size + 4 * rbn].view(np.uint32)
+    for rb in range(rbn):
+        blk = sexp.reshape(rbn, kbt * 64)[rb]
+        assert words[rb] == int(blk.min()) | (int(blk.max()) << 8), rb
 
 
 def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=None,

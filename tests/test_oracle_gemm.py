@@ -192,3 +192,35 @@ def test_hand_worked_example():
     expect_p = np.array([[int(v, 16) for v in row] for row in g["published_bf16"]],
                         dtype=np.uint16)
     assert np.array_equal(bits, expect_p)
+
+
+# Single products at the ends of the E8M0 range, worked out by hand:
+# (W code, W scale byte, x code, x scale byte, product, BF16 bits as rounded).
+#   0x01 = 2^-9 (smallest subnormal), 0x09 = 1.125 * 2^-6, 0x38 = 1.0,
+#   0x30 = 0.5, 0x78 = 256, 0x7E = 448, 0xB8 = -1.0; scale byte s = 2^(s-127).
+EXTREME_PRODUCTS = [
+    (0x01, 0, 0x38, 254, 2.0**-9, 0x3B00),            # 2^-136 * 2^127
+    (0x09, 0, 0x38, 254, 1.125 * 2.0**-6, 0x3C90),    # 1.125 * 2^-133 * 2^127
+    (0x7E, 247, 0x38, 0, 3.5, 0x4060),                # 448 * 2^120 * 2^-127
+    (0x78, 247, 0x30, 10, 1024.0, 0x4480),            # 2^128 * 2^-118
+    (0x38, 1, 0x38, 253, 2.0**0, 0x3F80),             # 2^-126 * 2^126
+    (0xB8, 57, 0x38, 57, -(2.0**-140), 0x8000),       # rounds to -0
+    (0x7E, 254, 0x7E, 254, 448.0**2 * 2.0**254, 0x7F80),  # beyond BF16: +inf
+]
+
+
+@pytest.mark.parametrize("wc,wsb,xc,xsb,value,bits", EXTREME_PRODUCTS)
+def test_extreme_scale_single_products(wc, wsb, xc, xsb, value, bits):
+    """The oracle decodes every scale byte exactly: one product at the E8M0
+    extremes has the value and the rounded bits worked out by hand, and the
+    published word clears a negative zero."""
+    w = np.zeros((8, 64), np.uint8)
+    x = np.zeros((1, 64), np.uint8)
+    ws = np.full((8, 2), 127, np.uint8)
+    xs = np.full((1, 2), 127, np.uint8)
+    w[3, 40], ws[3, 1], x[0, 40], xs[0, 1] = wc, wsb, xc, xsb
+    c, abs_sum = gemm.gemm_f64(w, ws, x, xs)
+    assert c[0, 3] == value and abs_sum[0, 3] == abs(value)
+    assert codecs.bf16_rne_bits(c)[0, 3] == bits
+    assert gemm.published_bits(c)[0, 3] == (0 if bits == 0x8000 else bits)
+    assert np.count_nonzero(c) == 1

@@ -123,6 +123,21 @@ def test_stress_structure():
         assert np.array_equal(p.xs[t], p.xs[t - 1])
 
 
+@pytest.mark.parametrize("m", [1, 8])
+def test_stress_tiny_rows_round_to_signed_zeros(m):
+    """The stress recipe's tiny rows: every result is a single product that
+    rounds to a BF16 zero, and some of them to negative zero, which the
+    publish must clear."""
+    from oracle import codecs, gemm
+
+    p = generate.random_problem(13 + m, m, 512, 1024, 4, "stress")
+    c, _ = gemm.gemm_f64(p.w, p.ws, p.x, p.xs)
+    raw = codecs.bf16_rne_bits(c[:, p.meta["tiny_rows"]])
+    assert np.all((raw & 0x7FFF) == 0)
+    assert np.any(raw == 0x8000)
+    assert np.all(gemm.published_bits(c[:, p.meta["tiny_rows"]]) == 0)
+
+
 def test_peer_payloads_hold_sentinels_and_negative_zeros():
     bits = generate.peer_payloads(1, 4, 8, 4096)
     assert bits.shape == (3, 8, 4096) and bits.dtype == np.uint16

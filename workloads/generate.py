@@ -11,8 +11,10 @@ optional split-K). These generators stand in for it with seeded Gaussian data:
   multiplied by 50 in every row before quantization.
 * "stress": some W rows are zero (half +0 codes, half -0 codes), odd tokens of
   x are the even tokens with the sign bit flipped, and a few "tiny" W rows hold
-  one smallest-subnormal e4m3 value with scale byte 0, so that their results
-  are about 2^-136 in magnitude and round to a BF16 zero of either sign.
+  one smallest-subnormal e4m3 value (2^-9) with scale byte 0, in a K column
+  where every token's value lies below 1.5 in magnitude, so that each of
+  their results is one product below 2^-135 in magnitude, which rounds to
+  a BF16 zero of the product's sign.
 * Peer payloads for emulated rank slots are BF16 bit patterns of Gaussians
   with about 1 % of halves forced to 0x8000 and some 32-bit words forced to
   0x80000000 (the Lamport sentinel), which the publish must turn into 0.
@@ -127,6 +129,8 @@ def _gaussian(rng: np.random.Generator, shape, std: float) -> np.ndarray:
 
 
 def _operands(rng, n, k, m, dist):
+    """(wq, ws, xq, xs, meta, x): the quantized operands and the float32
+    activation they come from."""
     if dist == "outliers":
         w = _gaussian(rng, (n, k), 0.02)
         x = _gaussian(rng, (m, k), 1.0)
@@ -139,11 +143,13 @@ def _operands(rng, n, k, m, dist):
         meta = {}
     wq, ws = quantize_mxfp8(w)
     xq, xs = quantize_mxfp8(x)
-    return wq, ws, xq, xs, meta
+    return wq, ws, xq, xs, meta, x
 
 
-def _stress(rng, wq, ws, xq, xs):
-    """Force exact zeros, negative zeros and BF16-underflowing results."""
+def _stress(rng, wq, ws, xq, xs, xf):
+    """Force exact zeros, negative zeros and BF16-underflowing results.
+    xf is the float32 activation before quantization; odd tokens become
+    copies of the even ones, so the even rows bound every token."""
     n, k = wq.shape
     m = xq.shape[0]
     rows = rng.choice(n, size=max(2, n // 64) + 8, replace=False)
@@ -151,9 +157,13 @@ def _stress(rng, wq, ws, xq, xs):
     half = len(zero_rows) // 2
     wq[zero_rows[:half]] = 0x00
     wq[zero_rows[half:]] = 0x80
+    # K columns whose activations all lie below 1.5 in magnitude (below
+    # 1.625 once quantized), so that 2^-136 times them stays under 2^-134,
+    # half of BF16's smallest step.
+    calm = np.flatnonzero(np.max(np.abs(xf[0::2]), axis=0) < 1.5)
     for r in tiny_rows:
         wq[r] = 0x00
-        k0 = int(rng.integers(k))
+        k0 = int(calm[rng.integers(calm.size)])
         wq[r, k0] = 0x01 if rng.integers(2) else 0x81
         ws[r] = 0
     for t in range(1, m, 2):
@@ -168,12 +178,37 @@ def random_problem(seed: int, m: int, n: int, k: int, split_k: int = 1,
                    dist: str = "normal", name: str | None = None) -> Problem:
     """A seeded problem of any shape ("normal", "outliers" or "stress")."""
     rng = np.random.default_rng(seed)
-    wq, ws, xq, xs, meta = _operands(rng, n, k, m, "outliers" if dist == "outliers"
-                                     else "normal")
+    wq, ws, xq, xs, meta, xf = _operands(rng, n, k, m, "outliers" if dist == "outliers"
+                                         else "normal")
     if dist == "stress":
-        meta.update(_stress(rng, wq, ws, xq, xs))
+        meta.update(_stress(rng, wq, ws, xq, xs, xf))
     return Problem(name or f"m{m}_n{n}_k{k}_s{split_k}_{dist}", m, n, k, split_k,
                    wq, ws, xq, xs, seed, meta)
+
+
+EXTREME_SCALE_TARGETS = (0, 1, 2, 3, 127, 246, 247, 250, 254)
+
+
+def extreme_scales(p: Problem, seed: int) -> Problem:
+    """A copy of p with its scale bytes moved to the ends of the E8M0 range.
+    Per 32-block column b, W's scale bytes lie at most 3 below a target that
+    cycles through EXTREME_SCALE_TARGETS (clamped to 0) and x's within 2 of
+    254 minus that target (clamped to 0..254), so each product is the codes'
+    product times 2^-5 .. 2^2, finite and far inside the FP32 range, while
+    both operands leave the range in which e4m3 * 2^(s-127) is a BF16 value."""
+    import copy
+
+    rng = np.random.default_rng(seed)
+    q = copy.deepcopy(p)
+    nb = p.k // BLOCK
+    target = np.array([EXTREME_SCALE_TARGETS[b % len(EXTREME_SCALE_TARGETS)]
+                       for b in range(nb)], dtype=np.int64)
+    ws = target[None, :] - rng.integers(0, 4, size=(p.n, nb))
+    xs = (254 - target)[None, :] + rng.integers(-2, 3, size=(p.m, nb))
+    q.ws = np.clip(ws, 0, 254).astype(np.uint8)
+    q.xs = np.clip(xs, 0, 254).astype(np.uint8)
+    q.name = p.name + "_extreme_scales"
+    return q
 
 
 def config_problem(index: int, m: int | None = None, split_k: int | None = None,
