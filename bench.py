@@ -69,6 +69,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--cold-mib", type=int, default=2048,
                     help="total size of the rotating W copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-warm", action="store_true",
+                    help="leave out the same-W (Infinity-Cache warm) pass, so that a profile of "
+                         "the run holds cold GEMM launches only")
     ap.add_argument("--cpu-calls", type=int, default=40)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before the timed steps, one plain device copy of this many MiB "
@@ -84,7 +87,8 @@ def parse() -> argparse.Namespace:
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_publish_n7168_k8192_m8_s4_hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "mxfp8_decode_gemm_amd", "csrc", f)
-                  for f in ("gemm_publish.hip", "mxgemm_internal.h", "quant_device.h")]
+                  for f in ("gemm_kernel.h", "gemm_publish.hip", "mxgemm_internal.h",
+                            "quant_device.h")]
 
 
 def strip_comments(src: str) -> str:
@@ -379,13 +383,15 @@ def headline(args) -> int:
     del run
     torch.cuda.empty_cache()
     # Same W every launch (Infinity-Cache resident): context, not the headline.
-    warm = Runner(p, split_k, 1, 114688, 0)
-    with torch.cuda.stream(warm.stream):
-        for i in range(3):
-            warm.step(i)
-        torch.cuda.synchronize()
-        warm_ms = gemm_only_ms(warm, K)
-    del warm
+    warm_ms = None
+    if not args.skip_warm:
+        warm = Runner(p, split_k, 1, 114688, 0)
+        with torch.cuda.stream(warm.stream):
+            for i in range(3):
+                warm.step(i)
+            torch.cuda.synchronize()
+            warm_ms = gemm_only_ms(warm, K)
+        del warm
 
     algo = p.algorithmic_bytes()
     achieved = algo / (kern_ms * 1e-3) / 1e9
@@ -412,7 +418,7 @@ def headline(args) -> int:
         "us_per_call": round(ms_step * 1e3, 3),
         "eager_us_per_call": round(eager_ms_step * 1e3, 3),
         "gemm_kernel_us": round(kern_ms * 1e3, 3),
-        "gemm_kernel_warm_us": round(warm_ms * 1e3, 3),
+        "gemm_kernel_warm_us": round(warm_ms * 1e3, 3) if warm_ms is not None else None,
         "gemm_launch_event_us": {"mean": round(float(np.mean(ext_ms)) * 1e3, 3),
                                  "min": round(min(ext_ms) * 1e3, 3),
                                  "max": round(max(ext_ms) * 1e3, 3)},

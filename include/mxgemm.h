@@ -136,14 +136,15 @@ int mxgemm_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
  *   ws_packed + ((rb*(k/128) + kb)*16 + r)*4
  *             = the 4 scale bytes w_scale[rb*16 + r][kb*4 .. +4)
  *   ws_packed + ceil(n/16)*16*(k/32) + 4*rb
- *             = the range word of row block rb: its smallest scale byte in
- *               bits 0-7, its largest in bits 8-15 (rows past n count as 127)
+ *             = the range word of row block rb: over its (row, 32-wide block)
+ *               pairs holding a nonzero code, the smallest scale byte in bits
+ *               0-7 and the largest in bits 8-15 (0xFF and 0 if none)
  * Rows past n are zero codes with scale byte 127. The transform is a one-time
  * re-layout at weight-load time (as FlashInfer's GEMM takes its own swizzled
  * scale layout on the publishing_gemm page); besides the range words it
  * moves bytes only. The GEMM reads the range words to know which row blocks
- * hold scale bytes outside 3..246, where an e4m3 value times its scale is no
- * longer a BF16 value (see mxgemm_publish).
+ * hold nonzero codes under scale bytes outside 3..246, where an e4m3 value
+ * times its scale is no longer a BF16 value (see mxgemm_publish).
  * Sizes: ceil(n/16)*16*k bytes, and ceil(n/16)*16*(k/32) plus
  * ceil(ceil(n/16)*4 / 16)*16 bytes; 0 on bad sizes. */
 size_t mxgemm_packed_weight_bytes(int32_t n, int32_t k);
@@ -193,14 +194,16 @@ int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int3
  * (2mn > capacity), MXG_EWORKSPACE, MXG_EUNSUPPORTED (the split-K grid cannot
  * be co-resident on this device), MXG_EHIP.
  *
- * Every scale byte 0..254 is taken (255 is the E8M0 NaN). A workgroup whose W
- * rows (their range words) or x slice hold a scale byte outside 3..246 runs
- * an exact path: the MFMA contracts the codes themselves, one 32-wide scale
- * block at a time, and each block's FP32 sum is multiplied by
- * 2^(sW + sX - 254); inside 3..246 each operand is converted with its scale
- * to an exact BF16 value first. Both are FP32 accumulations (FP32 subnormals
- * kept); a result or partial sum beyond the FP32 range is infinite or NaN on
- * either path, as FP32 accumulation gives.
+ * Every scale byte 0..254 is taken (255 is the E8M0 NaN). Inside 3..246 each
+ * operand is converted with its scale to an exact BF16 value and contracted
+ * in BF16 with FP32 accumulation. A workgroup whose W rows (their range
+ * words) or x slice hold a nonzero 32-wide block under a scale byte outside
+ * 3..246 (for BF16 x: a block quantized to scale byte 247 or more, the only
+ * quantized blocks whose values leave BF16) runs an exact path instead: the
+ * MFMA contracts the codes themselves, one 32-wide scale block at a time,
+ * and each block's FP32 sum is multiplied by 2^(sW + sX - 254). Both paths
+ * keep FP32 subnormals; a result or partial sum beyond the FP32 range is
+ * infinite or NaN on either, as FP32 accumulation gives.
  *
  * Failure: a split-K poll that gives up (see mxg_set_spin_limit) sets
  * MXG_ERR_SPLITK_SPIN in the workspace's ERROR word and leaves its packs

@@ -256,8 +256,11 @@ struct XStage {
   __device__ __forceinline__ bool scales_out() const {
     bool out = false;
     if constexpr (X16) {
+      // A chunk of zero codes contributes zeros at any scale.
 #pragma unroll
-      for (int i = 0; i < kChunks; ++i) out |= d[i] >= 0 && scale_byte_out(sc[i]);
+      for (int i = 0; i < kChunks; ++i)
+        out |= d[i] >= 0 && scale_byte_out(sc[i]) &&
+               ((v[i].x | v[i].y | v[i].z | v[i].w) & 0x7F7F7F7Fu) != 0;
     } else {
       out = (e0 >= 0 && scale_word_out(s0)) || (e1 >= 0 && scale_word_out(s1));
     }
@@ -327,7 +330,12 @@ struct XQuant {
       const uint32_t sb = block_scale_byte(quad_max(chunk_amax(v[i])));
       const uint2 codes = chunk_codes(v[i], sb);
       if (c < xch8) {
-        out |= scale_byte_out(sb);
+        // Codes quantized from BF16 values times their scale are multiples
+        // of 2^-133 (the grid of a BF16 input is never finer than e4m3's
+        // at its magnitude) with 4 significant bits: BF16 values, except
+        // where a code of 256 at scale byte 247 makes 2^128. Only the top
+        // end of the range leaves BF16 here.
+        out |= sb > kScaleHi;
         const int t = c / cpr8;
         const int q = c - t * cpr8;
         if constexpr (X16) {
@@ -474,8 +482,10 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
 
   // ---- W scale range of this wave's rows --------------------------------
   // mxgemm_pack_weight leaves one word per 16-row block after the tiles: the
-  // smallest scale byte in bits 0-7, the largest in bits 8-15. Loaded before
-  // the x loads, so waiting for x covers it.
+  // smallest and largest scale byte (bits 0-7, 8-15) of the block's 32-wide
+  // blocks that hold a nonzero code (0xFF and 0 when none does: a block of
+  // zero codes contributes zeros at any scale). Loaded before the x loads,
+  // so waiting for x covers it.
   const int KBT = K >> 7;         // K blocks per row block
   const int rbn = (N + 15) >> 4;  // packed row blocks
   uint32_t wrange[RB];

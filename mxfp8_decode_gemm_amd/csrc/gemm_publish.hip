@@ -50,24 +50,39 @@ __global__ void pack_weight_kernel(const uint8_t* w, const uint8_t* ws, int n, i
   }
 }
 
-// The word per 16-row block that follows the packed scale tiles: the
-// smallest scale byte of the block's tiles in bits 0-7, the largest in bits
-// 8-15 (the GEMM checks them against the range its main loop keeps exact).
-// One wave per row block, after pack_weight_kernel on the same stream; rows
-// past n hold 127, inside any range.
-__global__ void scale_summary_kernel(const uint8_t* wsp, int rbn, int kbt, uint32_t* summary) {
+// The word per 16-row block that follows the packed scale tiles: over the
+// block's (row, 32-wide K block) pairs that hold a nonzero code, the
+// smallest scale byte in bits 0-7 and the largest in bits 8-15 (0xFF and 0
+// when there is none). The GEMM checks them against the range its main loop
+// keeps exact; a block of zero codes contributes zeros at any scale. One wave
+// per row block, after pack_weight_kernel on the same stream. In a packed
+// tile, lane l's 16-byte pieces at 16 l and 1024 + 16 l hold row l % 16 and K
+// 16 (l / 16) .. +16 and 64 + 16 (l / 16) .. +16, so lanes l and l ^ 16 hold
+// the two halves of the 32-wide blocks l / 32 and 2 + l / 32 of row l % 16.
+__global__ void scale_summary_kernel(const uint8_t* wp, const uint8_t* wsp, int rbn, int kbt,
+                                     uint32_t* summary) {
   const int rb = blockIdx.x * (blockDim.x >> 6) + (int)(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (rb >= rbn) return;  // whole waves
-  const uint32_t* words = reinterpret_cast<const uint32_t*>(wsp) + (size_t)rb * kbt * 16;
   uint32_t lo = 255u, hi = 0u;
-  for (int u = lane; u < kbt * 16; u += 64) {
-    const uint32_t w = words[u];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t v = (w >> (8 * b)) & 0xFFu;
-      lo = v < lo ? v : lo;
-      hi = v > hi ? v : hi;
+  for (int kb = 0; kb < kbt; ++kb) {
+    const size_t t = (size_t)rb * kbt + kb;
+    const uint4 p0 = *reinterpret_cast<const uint4*>(wp + t * 2048 + 16 * lane);
+    const uint4 p1 = *reinterpret_cast<const uint4*>(wp + t * 2048 + 1024 + 16 * lane);
+    uint32_t nz0 = ((p0.x | p0.y | p0.z | p0.w) & 0x7F7F7F7Fu) != 0 ? 1u : 0u;
+    uint32_t nz1 = ((p1.x | p1.y | p1.z | p1.w) & 0x7F7F7F7Fu) != 0 ? 1u : 0u;
+    nz0 |= (uint32_t)__shfl_xor((int)nz0, 16, 64);
+    nz1 |= (uint32_t)__shfl_xor((int)nz1, 16, 64);
+    const uint32_t sw = reinterpret_cast<const uint32_t*>(wsp)[t * 16 + (lane & 15)];
+    const uint32_t s0 = (sw >> (8 * (lane >> 5))) & 0xFFu;
+    const uint32_t s1 = (sw >> (8 * (2 + (lane >> 5)))) & 0xFFu;
+    if (nz0) {
+      lo = s0 < lo ? s0 : lo;
+      hi = s0 > hi ? s0 : hi;
+    }
+    if (nz1) {
+      lo = s1 < lo ? s1 : lo;
+      hi = s1 > hi ? s1 : hi;
     }
   }
 #pragma unroll
@@ -278,8 +293,8 @@ hipError_t launch_pack_weight(const uint8_t* w, const uint8_t* ws, int n, int k,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rbn = (n + 15) / 16, kbt = k / 128;
-  hipLaunchKernelGGL(scale_summary_kernel, dim3((unsigned)((rbn + 3) / 4)), dim3(256), 0, s, wsp,
-                     rbn, kbt, reinterpret_cast<uint32_t*>(wsp + (size_t)rbn * kbt * 64));
+  hipLaunchKernelGGL(scale_summary_kernel, dim3((unsigned)((rbn + 3) / 4)), dim3(256), 0, s, wp,
+                     wsp, rbn, kbt, reinterpret_cast<uint32_t*>(wsp + (size_t)rbn * kbt * 64));
   return hipGetLastError();
 }
 

@@ -431,6 +431,12 @@ def test_pack_weight_layout(env, n, k):
     rng = np.random.default_rng(n + k)
     w = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
     ws = rng.integers(0, 256, size=(n, k // 32), dtype=np.uint8)
+    # 32-wide blocks of zero codes (+0 and -0) under extreme scale bytes: the
+    # range words leave them out
+    for j in range(0, n * (k // 32), 5):
+        r, b = divmod(j, k // 32)
+        w[r, 32 * b:32 * b + 32] = 0x80 if j % 2 else 0x00
+        ws[r, b] = 0 if j % 3 else 255
     wp, wsp = dv.pack_weight(dv.upload(w), dv.upload(ws), n, k)
     torch.cuda.synchronize()
     wp = wp.cpu().numpy()
@@ -456,12 +462,14 @@ def test_pack_weight_layout(env, n, k):
                     sexp[(t * 16 + r) * 4:(t * 16 + r) * 4 + 4] = ws[row, kb * 4:kb * 4 + 4]
     assert np.array_equal(wp, expect)
     assert np.array_equal(wsp[: sexp.size], sexp)
-    # one range word per row block: smallest and largest scale byte of its
-    # rows (rows past n count as 127)
+    # one range word per row block: smallest and largest scale byte over its
+    # (row, 32-wide block) pairs holding a nonzero code (0xFF and 0 if none)
     words = wsp[sexp.size: sexp.size + 4 * rbn].view(np.uint32)
+    nz = np.any((w & 0x7F).reshape(n, k // 32, 32) != 0, axis=2)
     for rb in range(rbn):
-        blk = sexp.reshape(rbn, kbt * 64)[rb]
-        assert words[rb] == int(blk.min()) | (int(blk.max()) << 8), rb
+        sel = ws[rb * 16:rb * 16 + 16][nz[rb * 16:rb * 16 + 16]]
+        lo, hi = (int(sel.min()), int(sel.max())) if sel.size else (0xFF, 0)
+        assert words[rb] == lo | (hi << 8), rb
 
 
 def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=None,
