@@ -466,18 +466,29 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
 
   // ---- call hand-off: generation and epoch ------------------------------
   // Read once per workgroup, before it counts itself (all_gather page,
-  // _AllGatherKernel.kernel: the last CTA to arrive advances the state). The
-  // loads are issued here and waited for only where the values are needed.
-  // The workspace's error word comes with the epoch: once a split-K poll
-  // has given up, its pairs can no longer be told from this call's, so no
-  // later call publishes until the workspace is armed again.
-  uint32_t gen = 0, epoch = 0, wserr = 0;
-  if (tid == hand_tid) {
+  // _AllGatherKernel.kernel: the last CTA to arrive advances the state).
+  // Without split-K one worker thread issues the generation load here and
+  // waits for it only where it stores it to LDS, after its x staging. With
+  // split-K the control wave reads the generation, the epoch and the
+  // workspace's error word (once a split-K poll has given up, its pairs can
+  // no longer be told from this call's, so no later call publishes until
+  // the workspace is armed again), stores them to LDS and stores its epoch
+  // word, all before the first barrier: a load still in flight where the
+  // control wave's path joins the workers' would make the workers wait for
+  // their whole W prologue at the first register they reuse.
+  uint32_t gen = 0, epoch = 0;
+  if (S == 1 && tid == hand_tid && a.state)
+    gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
+  if (S > 1 && tid == hand_tid) {
     if (a.state) gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
-    if (S > 1) {
-      epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH) + a.epoch_bias;
-      wserr = ld_agent_u32(a.ws_hdr + MXG_WS_ERROR);
-    }
+    epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH) + a.epoch_bias;
+    const uint32_t wserr = ld_agent_u32(a.ws_hdr + MXG_WS_ERROR);
+    hdr[0] = gen;
+    hdr[1] = epoch;
+    hdr[2] = wserr;
+    // This workgroup has read the epoch (the stored word is the value
+    // read, so the store is issued after the load returned).
+    st_agent_u32(a.flags + blockIdx.x, epoch);
   }
 
   // ---- W scale range of this wave's rows --------------------------------
@@ -617,14 +628,6 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
 
   // ---- control wave: epoch bookkeeping while the workers stream ---------
   if (S > 1 && ctl) {
-    if (tid == hand_tid) {
-      hdr[0] = gen;
-      hdr[1] = epoch;
-      hdr[2] = wserr;
-      // This workgroup has read the epoch (the stored word is the value
-      // read, so the store is issued after the load returned).
-      st_agent_u32(a.flags + blockIdx.x, epoch);
-    }
     if (blockIdx.x == 0) {
       // Every workgroup's word holding this call's epoch means every
       // workgroup has read it: only then may the next epoch be stored.
