@@ -377,6 +377,22 @@ int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* 
 #define MXG_STREAM_CHUNK_BYTES 32768
 int mxg_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement aid, not a step of the method: C[16][16] = sum over k of
+ * A[row][k] * 2^(as[row][k/32] - 127) * B[col][k] * 2^(bs[col][k/32] - 127)
+ * for e4m3fn A and B ([16][k] each, row-major, K contiguous) and their E8M0
+ * scales ([16][k/32] each), accumulated in FP32 by one wave in 128-wide K
+ * steps, into c[row * 16 + col] (FP32, device memory). scaled = 1 uses the
+ * block-scaled fp8 MFMA that the publishing_gemm page's MXFP8 linear layer
+ * runs (FlashInfer's mm_mxfp8, sf_vec_size 32); on gfx950 that is
+ * v_mfma_scale_f32_16x16x128_f8f6f4. scaled = 0 uses this library's GEMM
+ * arithmetic: each code times its scale converted to BF16 (exact for scale
+ * bytes 3..246), then v_mfma_f32_16x16x32_bf16. It exists so that the
+ * accuracy of the two on the same inputs can be compared on the device.
+ * k: a positive multiple of 128; all pointers 16-B aligned, scales may be
+ * any address. Errors: MXG_EINVAL, MXG_EALIGN, MXG_EHIP. */
+int mxg_probe_mfma(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+                   const uint8_t* b_scale, int32_t k, int32_t scaled, float* c, void* stream);
+
 /* Poll limit of the device spin loops (collect and split-K), in polls; the
  * loops back off with s_sleep between polls. Returns the previous limit.
  * A limit of 0 restores the default (2^20 polls). Process-wide. */

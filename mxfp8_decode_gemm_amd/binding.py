@@ -107,6 +107,7 @@ def _load() -> ctypes.CDLL:
         "mailbox_all_gather": (ctypes.c_int, [mbp, vp, vp, i64, vp]),
         "mxg_set_spin_limit": (u32, [u32]),
         "mxg_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
+        "mxg_probe_mfma": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, vp, vp]),
         "mxg_graph_begin": (ctypes.c_int, [vp]),
         "mxg_graph_end": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "mxg_graph_launch": (ctypes.c_int, [vp, vp]),
@@ -298,6 +299,11 @@ def mailbox_all_gather(mb: mxg_mailbox, src, out, nbytes: int, stream=None) -> N
 
 
 STREAM_CHUNK_BYTES = 32768
+
+
+def mxg_probe_mfma(a, a_scale, b, b_scale, k: int, scaled: bool, c, stream=None) -> None:
+    _check(_lib.mxg_probe_mfma(_ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), k,
+                               1 if scaled else 0, _ptr(c), _stream(stream)), "mxg_probe_mfma")
 
 
 def mxg_stream_read(src, nbytes: int, sink, stream=None) -> None:

@@ -293,6 +293,15 @@ int mxg_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream)
   return hip_code(launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
+int mxg_probe_mfma(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+                   const uint8_t* b_scale, int32_t k, int32_t scaled, float* c, void* stream) {
+  if (!a || !a_scale || !b || !b_scale || !c || k <= 0 || k % 128 || (scaled != 0 && scaled != 1))
+    return MXG_EINVAL;
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MXG_EALIGN;
+  return hip_code(launch_mfma_probe(a, a_scale, b, b_scale, k, scaled, c,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 uint32_t mxg_set_spin_limit(uint32_t polls) {
   return g_spin_limit.exchange(polls == 0 ? (1u << 20) : polls);
 }

@@ -89,6 +89,11 @@ hipError_t launch_quantize(const uint16_t* x, int rows, int k, uint8_t* xq, uint
 // MXG_STREAM_CHUNK_BYTES chunk into sink.
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
+// One wave's 16 x 16 x k product with the block-scaled fp8 MFMA (scaled) or
+// with the GEMM's BF16 conversion and BF16 MFMA (see mxg_probe_mfma).
+hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                             const uint8_t* bs, int k, int scaled, float* c, hipStream_t s);
+
 // Mailbox kernels.
 hipError_t launch_fill_u32(uint32_t* p, size_t words, uint32_t value, hipStream_t s);
 hipError_t launch_state_init(uint32_t* state, hipStream_t s);

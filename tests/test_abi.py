@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 25
+    assert len(names) == 26
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -243,3 +243,14 @@ def test_stream_read_validation(mx):
     assert lib.mxg_stream_read(4096, 64, 8194, None) == -2
     with open(os.path.join(ROOT, "include", "mxgemm.h")) as f:
         assert f"#define MXG_STREAM_CHUNK_BYTES {mx.STREAM_CHUNK_BYTES}" in f.read()
+
+
+def test_probe_mfma_validation(mx):
+    lib = mx.library()
+    assert lib.mxg_probe_mfma(None, 16, 4096, 16, 128, 0, 8192, None) == -1
+    assert lib.mxg_probe_mfma(4096, 16, 4096, 16, 0, 0, 8192, None) == -1
+    assert lib.mxg_probe_mfma(4096, 16, 4096, 16, 96, 0, 8192, None) == -1
+    assert lib.mxg_probe_mfma(4096, 16, 4096, 16, 128, 2, 8192, None) == -1
+    assert lib.mxg_probe_mfma(4096, 16, 4096, 16, 128, 1, None, None) == -1
+    assert lib.mxg_probe_mfma(4100, 16, 4096, 16, 128, 1, 8192, None) == -2
+    assert lib.mxg_probe_mfma(4096, 16, 4096, 16, 128, 1, 8196, None) == -2
