@@ -589,15 +589,14 @@ def collectives(args) -> int:
             mx.mxg_graph_destroy(g)
         st = mbx.state_words()
         state_ok = bool(st[mx.STATE_NEXT] == calls % 3 and st[mx.STATE_ERROR] == 0)
-        # bytes the consumer kernel moves: reads of every polled slot (and
-        # the caller's own input when fused), writes of the output and of the
-        # sentinel back into every polled slot
-        polled = ranks - 1 if op == "all_gather_fused" else ranks
+        # bytes the consumer kernel moves: reads of every polled slot, writes
+        # of the output and of the sentinel back into every polled slot; the
+        # fused all-gather also reads the caller's input and writes it into
+        # the caller's own slot before polling it
         if op == "all_reduce":
-            op_bytes = polled * nbytes + nbytes + polled * nbytes
+            op_bytes = ranks * nbytes + nbytes + ranks * nbytes
         else:
-            op_bytes = (polled * nbytes + (nbytes if op == "all_gather_fused" else 0)
-                        + ranks * nbytes + polled * nbytes)
+            op_bytes = (3 * ranks * nbytes + (2 * nbytes if op == "all_gather_fused" else 0))
         mean_us = float(np.mean(op_us))
         line = {"mode": "collectives", "op": op, "ranks": ranks, "nbytes_per_rank": nbytes,
                 "seed": seed, "call_us": round(call_us, 3),

@@ -319,15 +319,15 @@ int mailbox_publish_words(const mxg_mailbox* mb, int32_t rank, const void* src,
 
 /* Fused all-gather of one rank (all_gather page, module docstring, steps
  * 1-3; _AllGatherKernel.kernel), the caller being slot mb->rank: one kernel
- * writes the caller's payload `src` (nbytes, words equal to the sentinel
- * sent as 0) to out + rank * nbytes and, for every other rank r and pack
- * p < nbytes/16 of generation g = state[NEXT], polls the pack until none of
- * its words is the sentinel, writes it to out + (r * nbytes + 16 p), and
- * stores the sentinel back; the last workgroup sets state[NEXT] = (g+1) mod 3.
- * Equivalent to mailbox_publish_words(mb, mb->rank, src) followed by
- * mailbox_collect, except that the caller's own slot is never written (the
- * same thread would store, reload and reset it: same end state). Peers
- * publish with mailbox_publish_words before or during the call. The call
+ * stores the caller's payload `src` (nbytes, words equal to the sentinel
+ * sent as 0) into the caller's slot of generation g = state[NEXT] and, for
+ * every rank r, its own included, and pack p < nbytes/16 of generation g,
+ * polls the pack until none of its words is the sentinel, writes it to
+ * out + (r * nbytes + 16 p), and stores the sentinel back; the last
+ * workgroup sets state[NEXT] = (g+1) mod 3. Equivalent to
+ * mailbox_publish_words(mb, mb->rank, src) followed by mailbox_collect in
+ * one launch. Peers publish with mailbox_publish_words before or during the
+ * call. The call
  * takes the place of the caller's publish and collect for that generation:
  * nothing else may publish into the caller's own slot before it. `src` and
  * `out` are device memory, 16-B aligned; `out` holds ranks * nbytes bytes;

@@ -44,6 +44,9 @@ __device__ __forceinline__ void st_agent_u32(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint64_t ld_agent_u64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_agent_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
   const uint32_t lo = (w & 0xFFFFu) == 0x8000u ? 0u : (w & 0xFFFFu);
@@ -139,11 +142,13 @@ __global__ void publish_kernel(uint8_t* slot, int64_t gen_stride, uint32_t* stat
 // counts itself once after its generation load has returned (the count's
 // operand depends on the loaded word), so no workgroup of the launch can read
 // the advanced value. It also fuses the caller's own publish
-// (all_gather page, _AllGatherKernel):
-// the items of rank `self` come from `src` with sentinel words sent as 0,
-// straight to the output. The own slot is left untouched: publishing into it
-// and polling it back would be the same thread storing, reloading and
-// resetting its own pack, which ends in the same state.
+// (all_gather page, _AllGatherKernel, module docstring steps 1 and 2): an
+// item of rank `self` stores its pack of `src`, sentinel words sent as 0,
+// into its own slot of the generation with device-scope stores, then polls
+// that slot like every other rank's, its own included, copies it out and
+// resets it. On one GPU the poll returns the thread's own store; with peers
+// on other GPUs the same wait is what the page's own-slot poll is for, that
+// the rank's own copy has landed before it is read back.
 template <bool kGather>
 __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capacity, int ranks,
                                uint32_t* state, uint8_t* out, int64_t nbytes,
@@ -177,14 +182,15 @@ __global__ void collect_kernel(uint8_t* slots, int64_t gen_stride, int64_t capac
   for (int64_t i = i0; i < total; i += stride) {
     const int64_t r = i / packs;
     const int64_t p = i - r * packs;
-    if (kGather && r == self) {
-      *reinterpret_cast<uint4*>(out + r * nbytes + p * MXG_PACK_BYTES) =
-          sanitize_pack(*reinterpret_cast<const uint4*>(src + p * MXG_PACK_BYTES), true);
-      continue;
-    }
     uint64_t* slot = reinterpret_cast<uint64_t*>(base + r * capacity + p * MXG_PACK_BYTES);
     uint64_t lo, hi;
-    if (i == i0) {
+    if (kGather && r == self) {
+      const uint4 v = sanitize_pack(*reinterpret_cast<const uint4*>(src + p * MXG_PACK_BYTES), true);
+      st_agent_u64(slot, (uint64_t)v.x | ((uint64_t)v.y << 32));
+      st_agent_u64(slot + 1, (uint64_t)v.z | ((uint64_t)v.w << 32));
+      lo = ld_agent_u64(slot);
+      hi = ld_agent_u64(slot + 1);
+    } else if (i == i0) {
       lo = gen == 0 ? lo0 : (gen == 1 ? lo1 : lo2);
       hi = gen == 0 ? hi0 : (gen == 1 ? hi1 : hi2);
     } else {
