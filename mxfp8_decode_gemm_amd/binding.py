@@ -14,7 +14,9 @@ import os
 import re
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libmxgemm.so")
+# MXG_LIBRARY names another build of the same library to load (the host
+# sanitizer build of the ABI tests); the default is the in-tree build.
+LIB_PATH = os.environ.get("MXG_LIBRARY") or os.path.join(_PKG, "lib", "libmxgemm.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mxgemm.h")
 
 OK = 0

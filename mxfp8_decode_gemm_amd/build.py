@@ -79,5 +79,48 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C-ABI layer only (argument validation, size
+# arithmetic, descriptor handling): api.hip's host code is compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer (-Xarch_host: the device
+# code is built as usual) and linked with the regular objects of the other
+# sources. Loading it needs the ASan runtime preloaded (HOST_ASAN_RUNTIME).
+HOST_SAN_LIB = os.path.join(LIBDIR, "libmxgemm_hostsan.so")
+HOST_SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def host_asan_runtime() -> str:
+    """The clang ASan runtime of this ROCm toolchain (for LD_PRELOAD)."""
+    import glob
+
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("the clang ASan runtime was not found under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Build libmxgemm_hostsan.so (after build(): it reuses its objects)."""
+    hipcc = _hipcc()
+    srcs = sources()
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    api = os.path.join(CSRC, "api.hip")
+    san_obj = os.path.join(BUILD, "api.hostsan.o")
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g"]
+    _run([hipcc, *flags, *HOST_SAN_FLAGS, "-c", api, "-o", san_obj])
+    others = [o for s, o in zip(srcs, objs) if os.path.basename(s) != "api.hip"]
+    tmp = HOST_SAN_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *HOST_SAN_FLAGS, "-o", tmp, san_obj,
+          *others])
+    os.replace(tmp, HOST_SAN_LIB)
+    if verbose:
+        print(f"built {HOST_SAN_LIB}")
+    return HOST_SAN_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
