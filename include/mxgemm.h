@@ -217,10 +217,16 @@ int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int3
  * staged in LDS as BF16) is chosen from m, n, k, split_k and the device. Ring
  * depth and x staging leave the result bits unchanged; the number of waves
  * along K sets the FP32 summation order, so variants that differ there agree
- * to rounding, not bit for bit. For measurement and tests the environment
- * variable MXG_TILE="rb,wn,wk,depth[,xr[,x16]]" forces one variant
- * (MXG_EUNSUPPORTED when it is not built or does not fit), and MXG_X16=0
- * keeps x staged as FP8. */
+ * to rounding, not bit for bit. For measurement and tests mxgemm_tile runs
+ * the same GEMM with a chosen variant; the library reads no environment.
+ *
+ * Host state: the library keeps no configuration between calls except the
+ * poll limit of mxg_set_spin_limit (a process-wide debugging knob, read at
+ * launch; a deliberate departure from a fully stateless interface: the
+ * limit only decides when a wait that should never be long gives up) and
+ * memos of device queries (the default tile per shape and device, the
+ * resident-workgroup counts, the no-allocation scratch's device address),
+ * which change no result. */
 int mxgemm_publish(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
                    const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n,
                    int32_t k, int32_t split_k, void* workspace,
@@ -287,6 +293,24 @@ int mxgemm_publish_bf16(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* 
 int mxgemm(const uint8_t* w, const uint8_t* w_scale, const uint8_t* x, const uint8_t* x_scale,
            int32_t m, int32_t n, int32_t k, int32_t split_k, void* workspace,
            size_t workspace_bytes, uint16_t* c_out, void* stream);
+
+/* For tests and measurement, not for callers of the method: the GEMM of
+ * mxgemm_publish (mb and x, x_scale given), mxgemm_publish_bf16 (mb and
+ * x_bf16 given) or mxgemm (mb null, c_out required) run with a chosen
+ * kernel variant instead of the default one. `tile` is "fp8" (the default
+ * tile, the x slice kept as FP8 codes in LDS) or "rb,wn,wk,depth[,xr[,x16]]"
+ * (16*rb*wn-row tiles of wn*wk waves with `depth` K blocks of W in flight,
+ * xr staging rounds, x16 the BF16 x stage; see the variant table in
+ * gemm_kernel.h). Results are the same function of the inputs as with the
+ * default variant, within the stated tolerance; sum order may differ. The
+ * library reads no environment and keeps no override between calls: the
+ * variant applies to this call only. Errors: those of the form called, and
+ * MXG_EUNSUPPORTED when the variant is not built or does not fit. */
+int mxgemm_tile(const char* tile, const mxg_mailbox* mb, const uint8_t* w,
+                const uint8_t* w_scale, const uint8_t* x, const uint8_t* x_scale,
+                const uint16_t* x_bf16, int32_t m, int32_t n, int32_t k, int32_t split_k,
+                void* workspace, size_t workspace_bytes, uint16_t* c_out, uint8_t* x_q_out,
+                uint8_t* x_scale_out, void* stream);
 
 /* Stand-alone activation quantizer, the rule of mxgemm_publish_bf16:
  * [rows, k] BF16 `x` (device, 16-B aligned) -> e4m3fn codes `x_q` ([rows,

@@ -105,6 +105,8 @@ def _load() -> ctypes.CDLL:
         "mxgemm_publish_bf16": (ctypes.c_int, [mbp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp,
                                                vp, vp, vp]),
         "mxgemm": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp, vp]),
+        "mxgemm_tile": (ctypes.c_int, [ctypes.c_char_p, mbp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                       i32, vp, sz, vp, vp, vp, vp]),
         "mxfp8_quantize": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
         "mailbox_all_gather": (ctypes.c_int, [mbp, vp, vp, i64, vp]),
         "mxg_set_spin_limit": (u32, [u32]),
@@ -224,9 +226,37 @@ def mxgemm_pack_weight(w, w_scale, n: int, k: int, w_packed, ws_packed, stream=N
                                    _ptr(ws_packed), _stream(stream)), "mxgemm_pack_weight")
 
 
+# Kernel variant for the GEMM calls below (tests and measurement): None for
+# the library's default choice, else a tile spec of mxgemm_tile ("fp8" or
+# "rb,wn,wk,depth[,xr[,x16]]"); when set, mxgemm_publish, mxgemm_publish_bf16
+# and mxgemm go through mxgemm_tile with it. Python-side only: the library
+# itself keeps no such setting.
+TILE = None
+
+
+def _tile_call(mb, w, w_scale, x, x_scale, x_bf16, m, n, k, split_k, workspace,
+               workspace_bytes, c_out, x_q_out, x_scale_out, stream, what):
+    _check(_lib.mxgemm_tile(TILE.encode(), ctypes.byref(mb) if mb is not None else None,
+                            _ptr(w), _ptr(w_scale), _ptr(x), _ptr(x_scale), _ptr(x_bf16), m, n,
+                            k, split_k, _ptr(workspace), workspace_bytes, _ptr(c_out),
+                            _ptr(x_q_out), _ptr(x_scale_out), _stream(stream)), what)
+
+
+def mxgemm_tile(tile: str, mb, w, w_scale, x, x_scale, x_bf16, m: int, n: int, k: int,
+                split_k: int, workspace, workspace_bytes: int, c_out=None, x_q_out=None,
+                x_scale_out=None, stream=None) -> None:
+    _check(_lib.mxgemm_tile(tile.encode(), ctypes.byref(mb) if mb is not None else None,
+                            _ptr(w), _ptr(w_scale), _ptr(x), _ptr(x_scale), _ptr(x_bf16), m, n,
+                            k, split_k, _ptr(workspace), workspace_bytes, _ptr(c_out),
+                            _ptr(x_q_out), _ptr(x_scale_out), _stream(stream)), "mxgemm_tile")
+
+
 def mxgemm_publish(mb: mxg_mailbox, w, w_scale, x, x_scale, m: int, n: int, k: int,
                    split_k: int = 1, workspace=None, workspace_bytes: int = 0,
                    c_out=None, stream=None) -> None:
+    if TILE is not None:
+        return _tile_call(mb, w, w_scale, x, x_scale, None, m, n, k, split_k, workspace,
+                          workspace_bytes, c_out, None, None, stream, "mxgemm_publish")
     _check(_lib.mxgemm_publish(ctypes.byref(mb), _ptr(w), _ptr(w_scale), _ptr(x),
                                _ptr(x_scale), m, n, k, split_k, _ptr(workspace),
                                workspace_bytes, _ptr(c_out), _stream(stream)),
@@ -272,6 +302,10 @@ def mailbox_collect_sum(mb: mxg_mailbox, out, nbytes: int, stream=None) -> None:
 def mxgemm_publish_bf16(mb: mxg_mailbox, w, w_scale, x, m: int, n: int, k: int, split_k: int,
                         workspace, workspace_bytes: int, c_out=None, x_q_out=None,
                         x_scale_out=None, stream=None) -> None:
+    if TILE is not None:
+        return _tile_call(mb, w, w_scale, None, None, x, m, n, k, split_k, workspace,
+                          workspace_bytes, c_out, x_q_out, x_scale_out, stream,
+                          "mxgemm_publish_bf16")
     _check(_lib.mxgemm_publish_bf16(ctypes.byref(mb), _ptr(w), _ptr(w_scale), _ptr(x), m, n, k,
                                     split_k, _ptr(workspace), workspace_bytes, _ptr(c_out),
                                     _ptr(x_q_out), _ptr(x_scale_out), _stream(stream)),
@@ -280,6 +314,9 @@ def mxgemm_publish_bf16(mb: mxg_mailbox, w, w_scale, x, m: int, n: int, k: int, 
 
 def mxgemm(w, w_scale, x, x_scale, m: int, n: int, k: int, split_k: int, workspace,
            workspace_bytes: int, c_out, stream=None) -> None:
+    if TILE is not None:
+        return _tile_call(None, w, w_scale, x, x_scale, None, m, n, k, split_k, workspace,
+                          workspace_bytes, c_out, None, None, stream, "mxgemm")
     _check(_lib.mxgemm(_ptr(w), _ptr(w_scale), _ptr(x), _ptr(x_scale), m, n, k, split_k,
                        _ptr(workspace), workspace_bytes, _ptr(c_out), _stream(stream)),
            "mxgemm")

@@ -128,7 +128,7 @@ int gemm_call(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
               const uint8_t* x, const uint8_t* x_scale, const uint16_t* xb, int32_t m, int32_t n,
               int32_t k, int32_t split_k, void* workspace, size_t workspace_bytes,
               uint32_t epoch_bias, uint16_t* c_out, uint8_t* xq_out, uint8_t* xs_out,
-              void* stream, void* ev_start, void* ev_stop) {
+              void* stream, void* ev_start, void* ev_stop, const char* tile) {
   const int rc =
       gemm_validate(mb, w, w_scale, x, x_scale, xb, m, n, k, split_k, c_out, xq_out, xs_out);
   if (rc != MXG_OK) return rc;
@@ -142,7 +142,7 @@ int gemm_call(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MXG_EHIP;
   TileCfg cfg;
-  if (!choose_tile(m, n, k, split_k, &cfg)) return MXG_EUNSUPPORTED;
+  if (!choose_tile(m, n, k, split_k, tile, &cfg)) return MXG_EUNSUPPORTED;
 
   GemmArgs a;
   a.w = w;
@@ -213,6 +213,20 @@ int mxgemm(const uint8_t* w, const uint8_t* w_scale, const uint8_t* x, const uin
   if (!c_out) return MXG_EINVAL;
   return gemm_call(nullptr, w, w_scale, x, x_scale, nullptr, m, n, k, split_k, workspace,
                    workspace_bytes, 0, c_out, nullptr, nullptr, stream, nullptr, nullptr);
+}
+
+int mxgemm_tile(const char* tile, const mxg_mailbox* mb, const uint8_t* w,
+                const uint8_t* w_scale, const uint8_t* x, const uint8_t* x_scale,
+                const uint16_t* x_bf16, int32_t m, int32_t n, int32_t k, int32_t split_k,
+                void* workspace, size_t workspace_bytes, uint16_t* c_out, uint8_t* x_q_out,
+                uint8_t* x_scale_out, void* stream) {
+  if (!tile) return MXG_EINVAL;
+  if (!mb && !c_out) return MXG_EINVAL;             // the plain GEMM needs c_out
+  if (!mb && x_bf16) return MXG_EINVAL;             // BF16 x only with a publish
+  if (x_bf16 && (x || x_scale)) return MXG_EINVAL;  // one activation form
+  return gemm_call(mb, w, w_scale, x, x_scale, x_bf16, m, n, k, split_k, workspace,
+                   workspace_bytes, 0, c_out, x_q_out, x_scale_out, stream, nullptr, nullptr,
+                   tile);
 }
 
 int mxfp8_quantize(const uint16_t* x, int32_t rows, int32_t k, uint8_t* x_q, uint8_t* x_scale,

@@ -126,12 +126,14 @@ size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice) {
 
 bool tile_available(const TileCfg& c) { return find_variant(c, 1) != nullptr; }
 
-static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out);
+static bool choose_tile_uncached(int m, int n, int k, int split_k, const char* tile,
+                                 TileCfg* out);
 
-// The choice depends only on the sizes and the device: remembered per key.
-bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
-  if (std::getenv("MXG_TILE") || std::getenv("MXG_X16"))
-    return choose_tile_uncached(m, n, k, split_k, out);
+// The default choice depends only on the sizes and the device: remembered
+// per key (a memo of device queries, not state that changes a result). A
+// forced tile is not remembered.
+bool choose_tile(int m, int n, int k, int split_k, const char* tile, TileCfg* out) {
+  if (tile) return choose_tile_uncached(m, n, k, split_k, tile, out);
   static std::mutex mu;
   static std::map<std::tuple<int, int, int, int, int>, std::pair<bool, TileCfg>> cache;
   int dev = 0;
@@ -146,14 +148,15 @@ bool choose_tile(int m, int n, int k, int split_k, TileCfg* out) {
     }
   }
   TileCfg c{};
-  const bool ok = choose_tile_uncached(m, n, k, split_k, &c);
+  const bool ok = choose_tile_uncached(m, n, k, split_k, nullptr, &c);
   std::lock_guard<std::mutex> g(mu);
   cache[key] = std::make_pair(ok, c);
   *out = c;
   return ok;
 }
 
-static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out) {
+static bool choose_tile_uncached(int m, int n, int k, int split_k, const char* tile,
+                                 TileCfg* out) {
   const int ks = k / split_k;
   auto fits = [&](const TileCfg& c) {
     const Variant* v = find_variant(c, split_k);
@@ -177,22 +180,22 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, TileCfg* out)
   // 0.3-0.6 us faster on N=7168/K=2048/m=4, N=2048/K=8192/m=8/S=4 and
   // N=256/K=512/m=1 and on BF16 x, neutral on N=7168/K=8192/m=8/S=4, and
   // 3-4 us slower on N=4096/K=16384/S=8, where two workgroups share a CU.
-  // MXG_X16=0 keeps the FP8 stage.
+  // The tile spec "fp8" keeps the FP8 stage.
+  const bool keep_fp8 = tile && std::strcmp(tile, "fp8") == 0;
   auto upgrade_x16 = [&](TileCfg& c) {
-    const char* e = std::getenv("MXG_X16");
-    if (e && e[0] == '0') return;
+    if (keep_fp8) return;
     const long grid = (long)((n + tile_rows(c) - 1) / tile_rows(c)) * split_k;
     if (grid > cus) return;
     TileCfg c2 = c;
     c2.x16 = 1;
     if (fits(c2)) c = c2;
   };
-  if (const char* env = std::getenv("MXG_TILE")) {
-    // Measurement override: exactly this variant ("rb,wn,wk,depth[,xr[,x16]]",
-    // x16 chosen as usual when not given), or no launch at all.
+  if (tile && !keep_fp8) {
+    // Forced variant (mxgemm_tile): exactly "rb,wn,wk,depth[,xr[,x16]]", x16
+    // chosen as usual when not given, or no launch at all.
     TileCfg c{};
     const int got =
-        std::sscanf(env, "%d,%d,%d,%d,%d,%d", &c.rb, &c.wn, &c.wk, &c.depth, &c.xr, &c.x16);
+        std::sscanf(tile, "%d,%d,%d,%d,%d,%d", &c.rb, &c.wn, &c.wk, &c.depth, &c.xr, &c.x16);
     if (got == 4) c.xr = 1;
     if (got < 6) c.x16 = 0;
     if (got < 4 || (c.x16 != 0 && c.x16 != 1) || !fits(c)) return false;

@@ -61,10 +61,10 @@ inline int tile_threads(const TileCfg& c, int split_k) {
 // c.x16; the partial tile).
 size_t gemm_lds_bytes(const TileCfg& c, int m, int k_slice);
 
-// The tile for a problem; MXG_TILE="rb,wn,wk,depth[,xr[,x16]]" forces one
-// variant (and fails when it does not fit), MXG_X16=0 keeps x in FP8 in LDS.
-// Returns false when no variant fits.
-bool choose_tile(int m, int n, int k, int split_k, TileCfg* out);
+// The tile for a problem. tile null: the default choice; "fp8": the default
+// tile with x kept in FP8 in LDS; "rb,wn,wk,depth[,xr[,x16]]": exactly that
+// variant (fails when it does not fit). Returns false when no variant fits.
+bool choose_tile(int m, int n, int k, int split_k, const char* tile, TileCfg* out);
 
 // Whether a variant is compiled in.
 bool tile_available(const TileCfg& c);
@@ -129,6 +129,6 @@ int gemm_call(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale, c
               const uint8_t* x_scale, const uint16_t* xb, int32_t m, int32_t n, int32_t k,
               int32_t split_k, void* workspace, size_t workspace_bytes, uint32_t epoch_bias,
               uint16_t* c_out, uint8_t* xq_out, uint8_t* xs_out, void* stream, void* ev_start,
-              void* ev_stop);
+              void* ev_stop, const char* tile = nullptr);
 
 }  // namespace mxg

@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 26
+    assert len(names) == 27
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -254,3 +254,16 @@ def test_probe_mfma_validation(mx):
     assert lib.mxg_probe_mfma(4096, 16, 4096, 16, 128, 1, None, None) == -1
     assert lib.mxg_probe_mfma(4100, 16, 4096, 16, 128, 1, 8192, None) == -2
     assert lib.mxg_probe_mfma(4096, 16, 4096, 16, 128, 1, 8196, None) == -2
+
+
+def test_tile_validation(mx):
+    """mxgemm_tile: a tile spec is required, the plain form needs c_out, BF16
+    x only with a mailbox and never beside MXFP8 x; then mxgemm_publish's
+    validation (here: m out of range) before any HIP call."""
+    lib = mx.library()
+    args = [4096, 4096, 4096, 4096, None, 8, 256, 512, 1, None, 0, 8192, None, None, None]
+    assert lib.mxgemm_tile(None, None, *args) == -1
+    assert lib.mxgemm_tile(b"fp8", None, *args[:11], None, None, None, None) == -1
+    plain_bf16 = args[:2] + [None, None, 4096] + args[5:]
+    assert lib.mxgemm_tile(b"fp8", None, *plain_bf16) == -1
+    assert lib.mxgemm_tile(b"1,7,1,5", None, *(args[:5] + [0] + args[6:])) == -1

@@ -86,7 +86,7 @@ def test_negative_zero_reaches_the_epilogue(env, scales, split_k, x16, monkeypat
     their outputs. The raw output holds BF16 -0 (0x8000) for the negative ones
     and +0 for the positive ones; the mailbox holds 0x0000 for both."""
     if x16 == "0":
-        monkeypatch.setenv("MXG_X16", "0")
+        monkeypatch.setattr(env[0], "TILE", "fp8")
     from workloads.generate import Problem
 
     sw, sx = scales
@@ -153,7 +153,7 @@ def test_extreme_scales_single_products(env, mirror, split_k, x16, monkeypatch):
     """Scale bytes 0, 1, 2, 3, 246, 247 and 254 on W (or on x), each paired
     with a compensating partner: bit-exact against the oracle."""
     if x16 == "0":
-        monkeypatch.setenv("MXG_X16", "0")
+        monkeypatch.setattr(env[0], "TILE", "fp8")
     p = _extreme_singles(900 + 2 * split_k + mirror, mirror)
     p.split_k = split_k
     _say(f"case {p.name} split_k={split_k} x16={x16}")
@@ -169,7 +169,7 @@ def test_extreme_scales_dense(env, m, n, k, split_k, x16, monkeypatch):
     """Dense N(0,1) codes with scale bytes at both ends of the E8M0 range on
     both operands (workloads.generate.extreme_scales): within the tolerance."""
     if x16 == "0":
-        monkeypatch.setenv("MXG_X16", "0")
+        monkeypatch.setattr(env[0], "TILE", "fp8")
     from workloads import generate
 
     base = generate.random_problem(950 + m + split_k, m, n, k, split_k)

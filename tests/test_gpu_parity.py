@@ -121,7 +121,7 @@ def test_rows_and_ragged_n(env, m):
 
 
 # Every kernel variant of the library (rows-per-wave blocks, waves along
-# rows, waves along K, load depth), forced through the MXG_TILE override. The
+# rows, waves along K, load depth), forced through mxgemm_tile (binding.TILE). The
 # fifth field is the first staging round's size, the sixth whether x is also
 # kept as BF16 in LDS (without it: BF16 when it fits, the default).
 TILES = ["1,1,4,4", "1,1,8,4", "1,1,16,4", "1,4,1,8", "1,4,1,3", "1,7,1,8", "1,7,1,4",
@@ -147,7 +147,7 @@ def test_every_tile_variant(env, tile, monkeypatch):
     mx, _ = env
     from workloads import generate
 
-    monkeypatch.setenv("MXG_TILE", tile)
+    monkeypatch.setattr(mx, "TILE", tile)
     ran = 0
     for m, k, extreme in [(1, 2048, False), (5, 1024, False), (8, 2048, False),
                           (8, 8192, False), (3, 2048, True), (8, 8192, True)]:
@@ -168,10 +168,10 @@ def test_single_nonzero_sweep(env, x16, split, monkeypatch):
     """One nonzero W element and one nonzero x element at swept positions: the
     result is one exact product, so any slip of the MFMA lane, K-piece or
     scale mapping shows up bit for bit. With x kept as BF16 in LDS (the
-    default where it fits) and in FP8 (MXG_X16=0), with and without split-K."""
+    default where it fits) and in FP8 (tile spec "fp8"), with and without split-K."""
     mx, dv = env
     if x16 == "0":
-        monkeypatch.setenv("MXG_X16", "0")
+        monkeypatch.setattr(mx, "TILE", "fp8")
     codecs, gemm, _, _ = _oracle()
     from workloads.generate import Problem
 
