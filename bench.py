@@ -80,6 +80,9 @@ def parse() -> argparse.Namespace:
                     help="time every configuration (GPU and oracle), one JSON line each")
     ap.add_argument("--collectives", action="store_true",
                     help="time the mailbox consumers (all-gather, all-reduce), one line each")
+    ap.add_argument("--stream-sweep", action="store_true",
+                    help="the plain read of one packed W copy in every organisation "
+                         "mxg_stream_read_cfg offers, one line each")
     ap.add_argument("--activation-quant", action="store_true",
                     help="time the BF16-activation and unfused-publish variants, one line each")
     return ap.parse_args()
@@ -321,19 +324,104 @@ def gemm_only_ms(run: Runner, K: int) -> float:
                         timed=3)
 
 
-def stream_ms(run: Runner, K: int) -> tuple[float, int]:
-    """Per launch: a graph of K plain reads (mxg_stream_read) of the packed W
-    of the rotating copies, the same bytes the GEMM streams from HBM."""
+# The fastest organisation of the plain read found by --stream-sweep: one
+# workgroup per 32 KiB chunk, 512 threads, four nontemporal raw-buffer loads
+# of 16 bytes per thread in flight.
+BEST_STREAM = {"workgroups": 0, "threads": 512, "unroll": 4, "kind": 2, "interleave": False}
+
+
+def stream_ms(run: Runner, K: int, cfg: dict | None = None) -> tuple[float, int]:
+    """Per launch: a graph of K plain reads of the packed W of the rotating
+    copies, the same bytes the GEMM streams from HBM: mxg_stream_read, or
+    mxg_stream_read_cfg with `cfg`."""
     import torch
 
+    mx = run.mx
     nbytes = run.w[0][0].numel()
-    chunks = -(-nbytes // run.mx.STREAM_CHUNK_BYTES)
-    sink = torch.empty(chunks, dtype=torch.int32, device=run.w[0][0].device)
-    body = lambda: [run.mx.mxg_stream_read(run.w[i % run.copies][0], nbytes, sink, run.stream)
-                    for i in range(K)]
+    groups = (cfg or {}).get("workgroups") or -(-nbytes // mx.STREAM_CHUNK_BYTES)
+    sink = torch.empty(groups, dtype=torch.int32, device=run.w[0][0].device)
+    if cfg is None:
+        body = lambda: [mx.mxg_stream_read(run.w[i % run.copies][0], nbytes, sink, run.stream)
+                        for i in range(K)]
+    else:
+        body = lambda: [mx.mxg_stream_read_cfg(run.w[i % run.copies][0], nbytes, sink,
+                                               cfg["workgroups"], cfg["threads"], cfg["unroll"],
+                                               cfg["kind"], cfg["interleave"], run.stream)
+                        for i in range(K)]
     body()
     torch.cuda.synchronize()
     return run.graph_ms(body, K, timed=3), nbytes
+
+
+def stream_sweep(args) -> int:
+    """The plain HBM read of one packed W copy of N=7168 K=8192 (58720256
+    bytes) over the rotating cold copies, organised every way
+    mxg_stream_read_cfg offers: per launch, a graph of K reads, the median of
+    three timed replays. Each configuration's per-workgroup checksums are
+    checked against the host's XOR of copy 0 first."""
+    import numpy as np
+    import torch
+
+    from workloads import generate
+
+    p = generate.config_problem(2)
+    run = Runner(p, 1, 1, 2 * p.m * p.n, args.cold_mib)
+    mx = run.mx
+    nbytes = run.w[0][0].numel()
+    host = run.w[0][0].cpu().numpy().view(np.uint32)
+    chunk16 = mx.STREAM_CHUNK_BYTES // 16
+    n16 = nbytes // 16
+    K = min(args.steps, 100)
+
+    def expected(workgroups, interleave):
+        words = host.reshape(-1, 4)
+        if workgroups == 0 or interleave:
+            nch = -(-n16 // chunk16)
+            pad = np.zeros((nch * chunk16 - n16, 4), np.uint32)
+            per_chunk = np.bitwise_xor.reduce(
+                np.concatenate([words, pad]).reshape(nch, -1), axis=1)
+            if workgroups == 0:
+                return per_chunk
+            out = np.zeros(workgroups, np.uint32)
+            for g in range(min(workgroups, nch)):
+                out[g] = np.bitwise_xor.reduce(per_chunk[g::workgroups])
+            return out
+        per = -(-n16 // workgroups)
+        pad = np.zeros((per * workgroups - n16, 4), np.uint32)
+        return np.bitwise_xor.reduce(np.concatenate([words, pad]).reshape(workgroups, -1), axis=1)
+
+    configs = [(0, 256, 8, 0, 0)]
+    configs += [(0, t, u, k, 0) for t in (256, 512) for u in (4, 8, 16) for k in range(5)
+                if (t, u, k) != (256, 8, 0)]
+    configs += [(g, t, u, k, 0) for g in (256, 512, 1024, 2048) for t in (256, 512)
+                for u in (8, 16) for k in (0, 2, 4)]
+    configs += [(g, 256, u, k, 1) for g in (256, 512, 1024) for u in (8, 16) for k in (0, 2, 4)]
+    kinds = ["global_nt", "global", "buffer_nt", "buffer", "global_to_lds_nt"]
+    best = None
+    for (wg, threads, unroll, kind, inter) in configs:
+        groups = wg if wg else -(-nbytes // mx.STREAM_CHUNK_BYTES)
+        sink = torch.empty(groups, dtype=torch.int32, device="cuda")
+        mx.mxg_stream_read_cfg(run.w[0][0], nbytes, sink, wg, threads, unroll, kind, bool(inter),
+                               run.stream)
+        torch.cuda.synchronize()
+        ok = bool(np.array_equal(sink.cpu().numpy().view(np.uint32), expected(wg, inter)))
+        body = lambda: [mx.mxg_stream_read_cfg(run.w[i % run.copies][0], nbytes, sink, wg,
+                                               threads, unroll, kind, bool(inter), run.stream)
+                        for i in range(K)]
+        ms = run.graph_ms(body, K, timed=3)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        line = {"mode": "stream_sweep", "bytes": nbytes, "copies": run.copies,
+                "workgroups": wg if wg else f"{groups} (one per 32 KiB)", "threads": threads,
+                "loads_in_flight_per_thread": unroll, "load": kinds[kind],
+                "split": "chunks" if wg == 0 else ("interleaved chunks" if inter else "contiguous"),
+                "us": round(ms * 1e3, 3), "gbs": round(gbs, 1),
+                "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "checksums_ok": ok}
+        print(json.dumps(line), flush=True)
+        if ok and (best is None or gbs > best["gbs"]):
+            best = line
+    print(json.dumps({"mode": "stream_sweep_best", **{k: v for k, v in best.items()
+                                                      if k != "mode"}}), flush=True)
+    return 0
 
 
 def headline(args) -> int:
@@ -375,6 +463,7 @@ def headline(args) -> int:
         ext_ms = [a.elapsed_time(b) for a, b in kev]
         kern_ms = gemm_only_ms(run, K)
         read_ms, read_bytes = stream_ms(run, K)
+        best_ms, _ = stream_ms(run, K, BEST_STREAM)
         # Timed region: the K whole steps captured once as a HIP graph.
         ms_step = run.graph_ms(lambda: [run.step(i) for i in range(K)], K)
         state_ok = run.state_ok()
@@ -437,6 +526,14 @@ def headline(args) -> int:
             "us": round(read_ms * 1e3, 3),
             "gbs": round(read_bytes / (read_ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(read_bytes / (read_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "best_swept": {
+                "what": "the fastest read organisation of --stream-sweep (1 workgroup per "
+                        "32 KiB, 512 threads, 4 nontemporal buffer loads of 16 B in flight "
+                        "per thread), measured here",
+                "us": round(best_ms * 1e3, 3),
+                "gbs": round(read_bytes / (best_ms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(read_bytes / (best_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            },
         },
         "state_ok": state_ok,
     }
@@ -758,6 +855,8 @@ def main() -> int:
         return collectives(args)
     if args.activation_quant:
         return activation_quant(args)
+    if args.stream_sweep:
+        return stream_sweep(args)
     return all_configs(args) if args.all_configs else headline(args)
 
 

@@ -401,6 +401,24 @@ int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* 
 #define MXG_STREAM_CHUNK_BYTES 32768
 int mxg_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement aid, not a step of the method: the same plain read of `bytes`
+ * with the choices a streaming kernel makes exposed, to find what read
+ * organisation this device's HBM rewards. threads: 256 or 512 per
+ * workgroup; unroll: 4, 8 or 16 16-byte loads per thread in flight;
+ * load_kind: 0 global nontemporal, 1 global default policy, 2 raw buffer
+ * nontemporal, 3 raw buffer default policy (2 and 3: bytes at most
+ * 0x7FFF0000), 4 global straight into LDS (global_load_lds_dwordx4,
+ * nontemporal; each lane then reads its 16 bytes back from LDS); workgroups: 0 for one workgroup per MXG_STREAM_CHUNK_BYTES
+ * chunk, else that many workgroups, each reading one contiguous range of
+ * ceil(bytes/16 / workgroups) 16-byte words (interleave 0) or the chunks
+ * g, g + workgroups, ... (interleave 1, needs workgroups > 0). Workgroup g
+ * stores the XOR of every little-endian 32-bit word it read into sink[g];
+ * `sink` holds one word per workgroup. Errors: MXG_EINVAL, MXG_EALIGN,
+ * MXG_EHIP. */
+int mxg_stream_read_cfg(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                        int32_t threads, int32_t unroll, int32_t load_kind, int32_t interleave,
+                        void* stream);
+
 /* Measurement aid, not a step of the method: C[16][16] = sum over k of
  * A[row][k] * 2^(as[row][k/32] - 127) * B[col][k] * 2^(bs[col][k/32] - 127)
  * for e4m3fn A and B ([16][k] each, row-major, K contiguous) and their E8M0

@@ -112,6 +112,7 @@ def _load() -> ctypes.CDLL:
         "mxg_set_spin_limit": (u32, [u32]),
         "mxg_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
         "mxg_probe_mfma": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, vp, vp]),
+        "mxg_stream_read_cfg": (ctypes.c_int, [vp, sz, vp, i32, i32, i32, i32, i32, vp]),
         "mxg_graph_begin": (ctypes.c_int, [vp]),
         "mxg_graph_end": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "mxg_graph_launch": (ctypes.c_int, [vp, vp]),
@@ -343,6 +344,13 @@ STREAM_CHUNK_BYTES = 32768
 def mxg_probe_mfma(a, a_scale, b, b_scale, k: int, scaled: bool, c, stream=None) -> None:
     _check(_lib.mxg_probe_mfma(_ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), k,
                                1 if scaled else 0, _ptr(c), _stream(stream)), "mxg_probe_mfma")
+
+
+def mxg_stream_read_cfg(src, nbytes: int, sink, workgroups: int, threads: int, unroll: int,
+                        load_kind: int, interleave: bool, stream=None) -> None:
+    _check(_lib.mxg_stream_read_cfg(_ptr(src), nbytes, _ptr(sink), workgroups, threads, unroll,
+                                    load_kind, 1 if interleave else 0, _stream(stream)),
+           "mxg_stream_read_cfg")
 
 
 def mxg_stream_read(src, nbytes: int, sink, stream=None) -> None:

@@ -307,6 +307,23 @@ int mxg_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream)
   return hip_code(launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
+int mxg_stream_read_cfg(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                        int32_t threads, int32_t unroll, int32_t load_kind, int32_t interleave,
+                        void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 || bytes > ((size_t)1 << 40)) return MXG_EINVAL;
+  if (threads != 256 && threads != 512) return MXG_EINVAL;
+  if (unroll != 4 && unroll != 8 && unroll != 16) return MXG_EINVAL;
+  if (load_kind < 0 || load_kind > 4 || (interleave != 0 && interleave != 1)) return MXG_EINVAL;
+  if (workgroups < 0 || workgroups > 65536 || (interleave && workgroups == 0)) return MXG_EINVAL;
+  if ((load_kind == 2 || load_kind == 3) && bytes > (size_t)0x7FFF0000)
+    return MXG_EINVAL;  // one raw buffer
+  if (workgroups == 0 && (bytes + MXG_STREAM_CHUNK_BYTES - 1) / MXG_STREAM_CHUNK_BYTES > 0x7FFFFFFF)
+    return MXG_EINVAL;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return MXG_EALIGN;
+  return hip_code(launch_stream_read_cfg(src, bytes, sink, workgroups, threads, unroll, load_kind,
+                                         interleave, static_cast<hipStream_t>(stream)));
+}
+
 int mxg_probe_mfma(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
                    const uint8_t* b_scale, int32_t k, int32_t scaled, float* c, void* stream) {
   if (!a || !a_scale || !b || !b_scale || !c || k <= 0 || k % 128 || (scaled != 0 && scaled != 1))

@@ -89,6 +89,12 @@ hipError_t launch_quantize(const uint16_t* x, int rows, int k, uint8_t* xq, uint
 // MXG_STREAM_CHUNK_BYTES chunk into sink.
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
+// The configurable read stream of mxg_stream_read_cfg (arguments checked by
+// the caller).
+hipError_t launch_stream_read_cfg(const void* src, size_t bytes, uint32_t* sink, int workgroups,
+                                  int threads, int unroll, int kind, int interleave,
+                                  hipStream_t s);
+
 // One wave's 16 x 16 x k product with the block-scaled fp8 MFMA (scaled) or
 // with the GEMM's BF16 conversion and BF16 MFMA (see mxg_probe_mfma).
 hipError_t launch_mfma_probe(const uint8_t* a, const uint8_t* as, const uint8_t* b,

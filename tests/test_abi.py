@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 27
+    assert len(names) == 28
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -267,3 +267,25 @@ def test_tile_validation(mx):
     plain_bf16 = args[:2] + [None, None, 4096] + args[5:]
     assert lib.mxgemm_tile(b"fp8", None, *plain_bf16) == -1
     assert lib.mxgemm_tile(b"1,7,1,5", None, *(args[:5] + [0] + args[6:])) == -1
+
+
+def test_stream_read_cfg_validation(mx):
+    lib = mx.library()
+    ok = [4096, 65536, 8192, 0, 256, 8, 0, 0, None]
+    def call(**kw):
+        a = list(ok)
+        for i, name in enumerate(["src", "bytes", "sink", "wg", "threads", "unroll", "kind",
+                                  "inter", "stream"]):
+            if name in kw:
+                a[i] = kw[name]
+        return lib.mxg_stream_read_cfg(*a)
+    assert call(src=None) == -1
+    assert call(bytes=24) == -1
+    assert call(threads=128) == -1
+    assert call(unroll=2) == -1
+    assert call(kind=5) == -1
+    assert call(inter=1, wg=0) == -1
+    assert call(wg=-1) == -1
+    assert call(kind=2, bytes=0x80000000) == -1
+    assert call(src=4104) == -2
+    assert call(sink=8194) == -2
