@@ -83,6 +83,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--stream-sweep", action="store_true",
                     help="the plain read of one packed W copy in every organisation "
                          "mxg_stream_read_cfg offers, one line each")
+    ap.add_argument("--tile-sweep", default="",
+                    help="comma-separated configuration names (C0, C1, C2, C3-m1-s4, C4-A, "
+                         "... or all): every built GEMM variant's time on each")
     ap.add_argument("--activation-quant", action="store_true",
                     help="time the BF16-activation and unfused-publish variants, one line each")
     return ap.parse_args()
@@ -552,11 +555,22 @@ def headline(args) -> int:
     return 0
 
 
-def all_configs(args) -> int:
-    """Every configuration: GPU graph timings (whole step, GEMM+publish only,
-    the latter also with one W copy) and the oracle's time per call."""
+def launch_floor_ms(run: Runner, K: int) -> float:
+    """Per launch: a graph of K reads of 16 bytes by one workgroup
+    (mxg_stream_read): what any launch costs inside a graph here."""
     import torch
 
+    sink = torch.empty(1, dtype=torch.int32, device=run.w[0][0].device)
+    body = lambda: [run.mx.mxg_stream_read(run.w[i % run.copies][0], 16, sink, run.stream)
+                    for i in range(K)]
+    body()
+    torch.cuda.synchronize()
+    return run.graph_ms(body, K, timed=3)
+
+
+def config_cases():
+    """(name, problem, ranks, mailbox capacity, oracle calls) of every workload
+    configuration."""
     from workloads import generate
 
     cases = [("C0", generate.config_problem(0), 1, 512, 100),
@@ -568,8 +582,20 @@ def all_configs(args) -> int:
             cases.append((f"C3-m{m}-s{s}", generate.config_problem(3, m=m, split_k=s), 4, 65536, 3))
     for size in (0, 1):
         cases.append((f"C4-{'AB'[size]}", generate.config_problem(4, size=size), 4, 32768, 3))
+    return cases
+
+
+def all_configs(args) -> int:
+    """Every configuration: GPU graph timings (whole step, GEMM+publish only,
+    the latter also with one W copy), the plain read of the same W code bytes
+    over the same cold copies in its default and fastest swept forms, the
+    floor of one launch in a graph, and the oracle's time per call."""
+    import torch
+
+    from workloads import generate
+
     K = args.steps
-    for name, p, ranks, cap, cpu_calls in cases:
+    for name, p, ranks, cap, cpu_calls in config_cases():
         peers = generate.peer_payloads(p.seed, ranks, p.m, p.n) if ranks > 1 else None
         run = Runner(p, p.split_k, ranks, cap, args.cold_mib, peers)
         with torch.cuda.stream(run.stream):
@@ -579,6 +605,9 @@ def all_configs(args) -> int:
             kern_ms = gemm_only_ms(run, K)
             step_ms = run.graph_ms(lambda: [run.step(i) for i in range(K)], K, timed=3)
             ok = run.state_ok()
+            read_ms, read_bytes = stream_ms(run, K)
+            best_ms, _ = stream_ms(run, K, BEST_STREAM)
+            floor_ms = launch_floor_ms(run, K)
         del run
         torch.cuda.empty_cache()
         warm = Runner(p, p.split_k, ranks, cap, 0, peers)
@@ -596,13 +625,73 @@ def all_configs(args) -> int:
                 "gemm_gbs": round(algo / (kern_ms * 1e-3) / 1e9, 1),
                 "gemm_frac": round(algo / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "gemm_warm_us": round(warm_ms * 1e3, 3),
-                "step_us": round(step_ms * 1e3, 3), "state_ok": ok}
+                "step_us": round(step_ms * 1e3, 3), "state_ok": ok,
+                "read_bytes": read_bytes,
+                "read_us": round(min(read_ms, best_ms) * 1e3, 3),
+                "read_frac": round(read_bytes / (min(read_ms, best_ms) * 1e-3) / 1e9
+                                   / HBM_PEAK_GBS, 4),
+                "gemm_frac_of_read": round(algo / kern_ms / (read_bytes / min(read_ms, best_ms)), 4),
+                "launch_floor_us": round(floor_ms * 1e3, 3)}
         if not args.no_cpu_baseline:
             cpu, _ = cpu_baseline(p, cpu_calls, ranks, cap, peers)
             line["cpu_oracle_s_per_call"] = cpu["seconds_per_call"]
             line["cpu_cores"] = cpu["cores"]
             line["cpu_model"] = cpu["cpu_model"]
         print(json.dumps(line), flush=True)
+    return 0
+
+
+# Every built GEMM variant as a forced tile "rb,wn,wk,depth,xr,x16" (x16 = 1
+# only where the variant is built with x staged as BF16).
+SWEEP_TILES = ["1,1,4,4,1,0", "1,1,4,4,1,1", "1,1,8,4,1,0", "1,1,16,4,1,0", "1,4,1,8,1,0",
+               "1,4,1,3,1,0", "1,4,1,3,1,1", "1,7,1,8,1,0", "1,7,1,4,1,0", "1,7,1,3,1,0",
+               "1,7,1,3,1,1", "1,2,2,8,1,0", "1,2,2,8,1,1", "1,7,1,5,1,0", "1,7,1,5,1,1",
+               "1,2,2,5,1,0", "1,2,2,5,1,1", "1,4,2,8,1,0", "2,1,4,4,1,0", "1,8,1,8,1,0",
+               "2,2,2,4,1,0", "1,4,1,3,2,0"]
+
+
+def tile_sweep(args) -> int:
+    """GEMM+publish time (graph of K cold launches, median of three replays) of
+    every built variant that fits, per configuration, against the default
+    choice; one line per tile, then the best per configuration."""
+    import torch
+
+    from workloads import generate
+
+    wanted = set(args.tile_sweep.split(","))
+    K = args.steps
+    for name, p, ranks, cap, _ in config_cases():
+        if name not in wanted and "all" not in wanted:
+            continue
+        peers = generate.peer_payloads(p.seed, ranks, p.m, p.n) if ranks > 1 else None
+        run = Runner(p, p.split_k, ranks, cap, args.cold_mib, peers)
+        mx = run.mx
+        algo = p.algorithmic_bytes()
+        res = []
+        with torch.cuda.stream(run.stream):
+            for tile in [None] + SWEEP_TILES:
+                mx.TILE = tile
+                try:
+                    run.gemm(0)
+                    run.peers_and_collect()
+                except mx.MxgUnsupported:
+                    continue
+                torch.cuda.synchronize()
+                ms = gemm_only_ms(run, K)
+                ok = run.state_ok()
+                res.append((tile or "default", ms))
+                print(json.dumps({"mode": "tile_sweep", "config": name, "tile": tile or "default",
+                                  "gemm_us": round(ms * 1e3, 3),
+                                  "gemm_frac": round(algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "state_ok": ok}), flush=True)
+            mx.TILE = None
+        del run
+        torch.cuda.empty_cache()
+        best = min(res, key=lambda r: r[1])
+        default = [r for r in res if r[0] == "default"][0]
+        print(json.dumps({"mode": "tile_sweep_best", "config": name, "tile": best[0],
+                          "gemm_us": round(best[1] * 1e3, 3),
+                          "default_us": round(default[1] * 1e3, 3)}), flush=True)
     return 0
 
 
@@ -855,6 +944,8 @@ def main() -> int:
         return collectives(args)
     if args.activation_quant:
         return activation_quant(args)
+    if args.tile_sweep:
+        return tile_sweep(args)
     if args.stream_sweep:
         return stream_sweep(args)
     return all_configs(args) if args.all_configs else headline(args)

@@ -196,14 +196,18 @@ int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int3
  *
  * Every scale byte 0..254 is taken (255 is the E8M0 NaN). Inside 3..246 each
  * operand is converted with its scale to an exact BF16 value and contracted
- * in BF16 with FP32 accumulation. A workgroup whose W rows (their range
- * words) or x slice hold a nonzero 32-wide block under a scale byte outside
+ * in BF16 with FP32 accumulation. A 16-row block of W whose range word
+ * reaches outside 3..246 but spans at most 243 binades (say scale bytes
+ * 0..240, or 20..254) is converted with every scale byte moved by one shift
+ * s into 3..246 (exact), and its FP32 partial sums are multiplied by 2^-s
+ * once after the K loop. A workgroup whose W rows span more than that, or
+ * whose x slice holds a nonzero 32-wide block under a scale byte outside
  * 3..246 (for BF16 x: a block quantized to scale byte 247 or more, the only
- * quantized blocks whose values leave BF16) runs an exact path instead: the
+ * quantized blocks whose values leave BF16), runs an exact path instead: the
  * MFMA contracts the codes themselves, one 32-wide scale block at a time,
- * and each block's FP32 sum is multiplied by 2^(sW + sX - 254). Both paths
+ * and each block's FP32 sum is multiplied by 2^(sW + sX - 254). All paths
  * keep FP32 subnormals; a result or partial sum beyond the FP32 range is
- * infinite or NaN on either, as FP32 accumulation gives.
+ * infinite or NaN on any, as FP32 accumulation gives.
  *
  * Failure: a split-K poll that gives up (see mxg_set_spin_limit) sets
  * MXG_ERR_SPLITK_SPIN in the workspace's ERROR word and leaves its packs

@@ -113,9 +113,13 @@ constexpr int kHdrFlags = 4;
 // 2^(s-136), which BF16's smallest step 2^-133 divides for s >= 3; the
 // largest, 448 * 2^(s-127) = 1.75 * 2^(s-119), stays below BF16's largest
 // finite 1.9921875 * 2^127 for s <= 246. Inside this range the main loop
-// converts each operand with its scale; a workgroup that meets a scale byte
-// outside it takes the exact path (products of the codes, each 32-wide
-// block's sum scaled by 2^(sW + sX - 254) in FP32).
+// converts each operand with its scale. A W row block whose scale bytes
+// leave the range but span at most kScaleHi - kScaleLo binades stays in the
+// main loop with all its scales moved into the range by one shift, undone
+// on its partial sums after the loop. A workgroup that meets any other
+// scale byte outside the range (an x scale byte, or a W row block spanning
+// more) takes the exact path (products of the codes, each 32-wide block's
+// sum scaled by 2^(sW + sX - 254) in FP32).
 constexpr uint32_t kScaleLo = 3;
 constexpr uint32_t kScaleHi = 246;
 
@@ -500,6 +504,9 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   const int KBT = K >> 7;         // K blocks per row block
   const int rbn = (N + 15) >> 4;  // packed row blocks
   uint32_t wrange[RB];
+  int wshift[RB];  // the scale shift of each row block (0 inside the exact range)
+#pragma unroll
+  for (int i = 0; i < RB; ++i) wshift[i] = 0;
   if (!ctl) {
     const uint32_t* wsum = reinterpret_cast<const uint32_t*>(a.ws + (size_t)rbn * KBT * 64);
 #pragma unroll
@@ -603,12 +610,21 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
                                         XStage<NT, XR>::kWords * NT);
     }
     // Range flags of this wave. The W summary is pinned here so that its
-    // use, and so the wait for it, stays behind the W prologue.
+    // use, and so the wait for it, stays behind the W prologue. A row block
+    // whose scale bytes reach outside the exact range but span at most
+    // kScaleHi - kScaleLo binades keeps the main loop: its operands are
+    // converted with every scale moved by one shift into the range (exact),
+    // and its partial sums are scaled back by 2^-shift once, after the loop.
+    // Only a wider span sends the workgroup to the exact path.
     bool wout = false;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       asm volatile("" : "+v"(wrange[i]));
-      wout |= (wrange[i] & 0xFFu) < kScaleLo || ((wrange[i] >> 8) & 0xFFu) > kScaleHi;
+      const int lo = (int)(wrange[i] & 0xFFu), hi = (int)((wrange[i] >> 8) & 0xFFu);
+      const int sh = lo < (int)kScaleLo ? (int)kScaleLo - lo
+                                        : (hi > (int)kScaleHi ? (int)kScaleHi - hi : 0);
+      wout |= sh != 0 && hi - lo > (int)(kScaleHi - kScaleLo);
+      wshift[i] = sh;
     }
     const uint32_t fl = (__any(xout) ? 1u : 0u) | (wout ? 2u : 0u);
     if (lane == 0) hdr[kHdrFlags + wave] = fl;
@@ -674,6 +690,12 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   v4f acc[RB];
 #pragma unroll
   for (int i = 0; i < RB; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  // 2^(shift - 127) per row block: ldexp of it by a scale byte is the
+  // shifted scale (a normal or subnormal FP32 value for shifts -9 .. 3).
+  float wbase[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+    wbase[i] = __builtin_amdgcn_ldexpf(__uint_as_float(0x00400000u), wshift[i]);
   const bool tok = r16 < m;
   const int xrow = tok ? r16 : 0;  // x row this lane's B operand reads
   const uint4* xbp = xl + grp * m + xrow;  // X16: this lane's first BF16 piece
@@ -702,8 +724,9 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const float fa0 = e8m0_to_f32((wsc[d][i] >> (8 * sb0)) & 0xFFu);
-      const float fa1 = e8m0_to_f32((wsc[d][i] >> (8 * (sb0 + 2))) & 0xFFu);
+      const float fa0 = __builtin_amdgcn_ldexpf(wbase[i], (int)((wsc[d][i] >> (8 * sb0)) & 0xFFu));
+      const float fa1 =
+          __builtin_amdgcn_ldexpf(wbase[i], (int)((wsc[d][i] >> (8 * (sb0 + 2))) & 0xFFu));
       const v8bf a0 = fp8x8_to_bf16(wlo[d][i].x, wlo[d][i].y, fa0);
       const v8bf a1 = fp8x8_to_bf16(wlo[d][i].z, wlo[d][i].w, fa0);
       const v8bf a2 = fp8x8_to_bf16(whi[d][i].x, whi[d][i].y, fa1);
@@ -723,43 +746,34 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   // ascending K. Lane l's four results are rows 4 (l / 16) + r of the row
   // block and token l % 16; row r's scale word comes from lane 4 (l / 16) + r,
   // which loaded it. The W pieces come from the same ring as consume's.
-  auto consume_exact = [&](int d, int j) __attribute__((always_inline)) {
+  auto consume_exact = [&](const v4u (&ewl)[RB], const v4u (&ewh)[RB], const uint32_t (&ews)[RB],
+                           int j) __attribute__((always_inline)) {
     const int kb = kb_lo + j;
     const uint4 xlo = xl[((kb * 2 + 0) * 4 + grp) * m + xrow];
     const uint4 xhi = xl[((kb * 2 + 1) * 4 + grp) * m + xrow];
     const uint32_t xsw = *reinterpret_cast<const uint32_t*>(xsl + xrow * kspw + kb * 4);
     const bool lo = grp < 2;
     const v8bf z = {};
-    const v8bf b0 = fp8x8_to_bf16(xlo.x, xlo.y, 1.0f);
-    const v8bf b1 = fp8x8_to_bf16(xlo.z, xlo.w, 1.0f);
-    const v8bf b2 = fp8x8_to_bf16(xhi.x, xhi.y, 1.0f);
-    const v8bf b3 = fp8x8_to_bf16(xhi.z, xhi.w, 1.0f);
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const v4u wl = wlo[d][i];
-      const v4u wh = whi[d][i];
-      const uint32_t sw = wsc[d][i];
-      const v8bf a0 = fp8x8_to_bf16(wl.x, wl.y, 1.0f);
-      const v8bf a1 = fp8x8_to_bf16(wl.z, wl.w, 1.0f);
-      const v8bf a2 = fp8x8_to_bf16(wh.x, wh.y, 1.0f);
-      const v8bf a3 = fp8x8_to_bf16(wh.z, wh.w, 1.0f);
-      v4f t[4];
-      t[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, lo ? b0 : z, zero, 0, 0, 0);
-      t[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, lo ? b1 : z, t[0], 0, 0, 0);
-      t[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, lo ? z : b0, zero, 0, 0, 0);
-      t[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, lo ? z : b1, t[1], 0, 0, 0);
-      t[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, lo ? b2 : z, zero, 0, 0, 0);
-      t[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, lo ? b3 : z, t[2], 0, 0, 0);
-      t[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, lo ? z : b2, zero, 0, 0, 0);
-      t[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, lo ? z : b3, t[3], 0, 0, 0);
+      const uint32_t sw = ews[i];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t swr = (uint32_t)__shfl((int)sw, 4 * grp + r, 64);
+      for (int b = 0; b < 4; ++b) {
+        const v4u wv = b < 2 ? ewl[i] : ewh[i];
+        const uint4 xv = b < 2 ? xlo : xhi;
+        const bool mine = (b & 1) ? !lo : lo;
+        const v8bf a0 = fp8x8_to_bf16(wv.x, wv.y, 1.0f);
+        const v8bf a1 = fp8x8_to_bf16(wv.z, wv.w, 1.0f);
+        const v8bf x0 = fp8x8_to_bf16(xv.x, xv.y, 1.0f);
+        const v8bf x1 = fp8x8_to_bf16(xv.z, xv.w, 1.0f);
+        v4f t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, mine ? x0 : z, zero, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, mine ? x1 : z, t, 0, 0, 0);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t swr = (uint32_t)__shfl((int)sw, 4 * grp + r, 64);
           const int e = (int)((swr >> (8 * b)) & 0xFFu) + (int)((xsw >> (8 * b)) & 0xFFu) - 254;
-          acc[i][r] += __builtin_amdgcn_ldexpf(t[b][r], e);
+          acc[i][r] += __builtin_amdgcn_ldexpf(t[r], e);
         }
       }
     }
@@ -784,10 +798,39 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
       }
     }
   };
-  if (exact_path)
-    stream(consume_exact);
-  else
+  if (exact_path) {
+    // The prologue's ring is let land and dropped; the exact stream keeps
+    // two blocks in flight in registers of its own.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    v4u el[2][RB], eh[2][RB];
+    uint32_t es[2][RB];
+    auto eload = [&](int d, int j) __attribute__((always_inline)) {
+      const int vo = j >= 0 ? 16 * lane : kPastBuffer;
+      const int so = j >= 0 ? 4 * r16 : kPastBuffer;
+      const int jo = j >= 0 ? j : 0;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        el[d][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs[i], vo, jo * 2048, kLoadNontemporal);
+        eh[d][i] = __builtin_amdgcn_raw_buffer_load_b128(wrs[i], vo + 1024, jo * 2048, kLoadNontemporal);
+        es[d][i] = __builtin_amdgcn_raw_buffer_load_b32(srs[i], so, jo * 64, 0);
+      }
+    };
+    eload(0, nbw > 0 ? 0 : -1);
+    eload(1, nbw > 1 ? 1 : -1);
+    for (int j0 = 0; j0 < nbw; j0 += 2) {
+      consume_exact(el[0], eh[0], es[0], j0);
+      eload(0, j0 + 2 < nbw ? j0 + 2 : -1);
+      if (j0 + 1 < nbw) consume_exact(el[1], eh[1], es[1], j0 + 1);
+      eload(1, j0 + 3 < nbw ? j0 + 3 : -1);
+    }
+  } else {
     stream(consume);
+    // Undo the row blocks' scale shifts: one rounding, FP32 subnormals kept.
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][r] = __builtin_amdgcn_ldexpf(acc[i][r], -wshift[i]);
+  }
 
   // ---- roles after the main loop ---------------------------------------
   // Each 16-byte pack (8 columns of one token) is reduced by one slice: in

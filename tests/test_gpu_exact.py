@@ -6,11 +6,13 @@
   module docstring: every output is published with negative zero cleared).
 * The whole E8M0 range (publishing_gemm page, PublishingMxfp8Linear._compile:
   one Float8E8M0FNU scale per 32 values). Scale bytes 0..2 and 247..254 make
-  e4m3 times 2^(s-127) leave the BF16 range. Such workgroups take the exact
-  path: MFMA on the codes, one scale block at a time, then ldexp. Single
-  products are exact there, so the device must match the oracle bit for bit.
-  Dense problems with scale bytes at both ends on both operands must match
-  within the tolerance.
+  e4m3 times 2^(s-127) leave the BF16 range. A W row block that leaves it
+  at one end only is shifted into it and scaled back after the K loop; any
+  other such workgroup takes the exact path: MFMA on the codes, one scale
+  block at a time, then ldexp. Single products are exact on both, so the
+  device must match the oracle bit for bit. Dense problems with scale bytes
+  at both ends (both operands, or shifted W row blocks) must match within
+  the tolerance.
 * BF16 activations near the BF16 maximum, whose quantized scale byte is 247
   with codes up to 256 (2^128 after scaling).
 * A split-K poll that gives up leaves the workspace failed: nothing is
@@ -160,6 +162,92 @@ def test_extreme_scales_single_products(env, mirror, split_k, x16, monkeypatch):
     raw, got, _ = _publish(env, p, split_k)
     _check(raw, got, p, bitwise=True)
     assert np.count_nonzero(raw) == p.n  # one nonzero result per row
+
+
+LOW_BLOCK = [0, 1, 2, 3, 50, 120, 200, 240]
+HIGH_BLOCK = [247, 250, 254, 246, 200, 120, 60, 14]
+
+
+def _shifted_singles(seed, m=8, n=128, k=2048):
+    """16-row blocks of W alternate between scale bytes reaching below the
+    exact range (0, 1, 2 beside in-range bytes up to 240) and above it (247,
+    250, 254 beside in-range bytes down to 14). Each block spans at most 240
+    binades, so it stays in the main loop with one shift. Row r has one
+    nonzero W code in its own 32-block, times one nonzero x code of token
+    r % m whose scale byte (kept inside 3..246) puts the product near 2^0:
+    a normal number with at most 8 significant bits, so exact."""
+    from workloads.generate import Problem
+
+    rng = np.random.default_rng(seed)
+    w = np.zeros((n, k), np.uint8)
+    x = np.zeros((m, k), np.uint8)
+    ws = np.full((n, k // 32), 127, np.uint8)
+    xs = np.full((m, k // 32), 127, np.uint8)
+    pool = np.r_[np.arange(0x01, 0x08), np.arange(0x08, 0x20), np.arange(0x70, 0x7F)]
+    for r in range(n):
+        b = r % (k // 32)
+        kk = 32 * b + int(rng.integers(32))
+        t = r % m
+        group = LOW_BLOCK if (r // 16) % 2 == 0 else HIGH_BLOCK
+        s_w = group[r % len(group)]
+        s_x = int(np.clip(254 - s_w + rng.integers(-3, 4), 3, 246))
+        w[r, kk] = int(rng.choice(pool)) | (0x80 if rng.integers(2) else 0)
+        x[t, kk] = int(rng.choice(pool)) | (0x80 if rng.integers(2) else 0)
+        ws[r, b], xs[t, b] = s_w, s_x
+    return Problem("shifted_singles", m, n, k, 1, w, ws, x, xs, seed)
+
+
+@pytest.mark.parametrize("x16", ["auto", "0"])
+@pytest.mark.parametrize("split_k", [1, 4])
+def test_shifted_row_blocks_single_products(env, split_k, x16, monkeypatch):
+    """W row blocks whose scale bytes leave 3..246 at one end only: bit-exact
+    against the oracle (the shift and its undoing lose nothing here)."""
+    if x16 == "0":
+        monkeypatch.setattr(env[0], "TILE", "fp8")
+    p = _shifted_singles(970 + split_k)
+    p.split_k = split_k
+    _say(f"case {p.name} split_k={split_k} x16={x16}")
+    raw, got, _ = _publish(env, p, split_k)
+    _check(raw, got, p, bitwise=True)
+    assert np.count_nonzero(raw) == p.n
+
+
+@pytest.mark.parametrize("x16", ["auto", "0"])
+@pytest.mark.parametrize("m,n,k,split_k", [(8, 1000, 2048, 1), (8, 1000, 2048, 4),
+                                           (1, 512, 4096, 8)])
+def test_shifted_row_blocks_dense(env, m, n, k, split_k, x16, monkeypatch):
+    """Dense N(0,1) codes. Even 16-row blocks of W take scale bytes 0..5
+    everywhere (their results sit around BF16's subnormals); odd ones take
+    247..254 in every fourth 32-block column and 100..119 elsewhere. x takes
+    scale bytes 3..6 in those columns (so the large products stay near 2^0)
+    and 118..122 elsewhere, always inside 3..246. Every W row block leaves
+    3..246 at one end only: the shifted main loop, within the tolerance."""
+    if x16 == "0":
+        monkeypatch.setattr(env[0], "TILE", "fp8")
+    from workloads import generate
+
+    p = generate.random_problem(980 + m + split_k, m, n, k, split_k)
+    rng = np.random.default_rng(981 + m)
+    nb = k // 32
+    hi_col = np.arange(nb) % 4 == 0
+    ws = np.empty((n, nb), np.int64)
+    for rb in range(0, n, 16):
+        rows = slice(rb, min(rb + 16, n))
+        cnt = rows.stop - rb
+        if (rb // 16) % 2 == 0:
+            ws[rows] = rng.integers(0, 6, size=(cnt, nb))
+        else:
+            ws[rows] = np.where(hi_col, 247 + rng.integers(0, 8, size=(cnt, nb)),
+                                100 + rng.integers(0, 20, size=(cnt, nb)))
+    xs = np.where(hi_col, 3 + rng.integers(0, 4, size=(m, nb)),
+                  118 + rng.integers(0, 5, size=(m, nb)))
+    p.ws = ws.astype(np.uint8)
+    p.xs = xs.astype(np.uint8)
+    assert p.ws.min() <= 2 and p.ws.max() >= 247 and 3 <= p.xs.min() and p.xs.max() <= 246
+    _say(f"case shifted_dense m={m} n={n} k={k} split_k={split_k} x16={x16}")
+    raw, got, _ = _publish(env, p, split_k)
+    exact = _check(raw, got, p, bitwise=False)
+    assert np.all(np.isfinite(exact))
 
 
 @pytest.mark.parametrize("x16", ["auto", "0"])
