@@ -138,6 +138,13 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kPastBuffer = 0x40000000;
 constexpr int kLoadNontemporal = 2;
 
+// A word that nothing writes while the kernel runs, read at a wave-uniform
+// address through the constant address space: a scalar load, counted apart
+// from the vector loads of the W stream, so a wait for it never waits for
+// the stream (the dispatch's acquire makes earlier launches' stores visible).
+__device__ __forceinline__ uint32_t ld_uniform_u32(const uint32_t* p) {
+  return *(const __attribute__((address_space(4))) uint32_t*)(p);
+}
 __device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -166,6 +173,16 @@ __device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w) {
   return lo | hi;
 }
 
+// Token row of index c in a slice of rows of d items each (c < 8 d: an
+// activation has at most 8 rows): seven compares against multiples of the
+// wave-uniform d instead of an integer division.
+__device__ __forceinline__ int row_of(int c, int d) {
+  int t = 0;
+#pragma unroll
+  for (int j = 1; j < 8; ++j) t += c >= j * d ? 1 : 0;
+  return t;
+}
+
 // Copies x chunks (16 bytes) of the workgroup's K slice into LDS in the order
 // the MFMA B operand reads them: chunk (kb, half, group, t) holds
 // x[t][kb*128 + 64*half + 16*group .. +16).
@@ -183,7 +200,7 @@ struct XStage {
   int e0, e1;
 
   __device__ __forceinline__ static int dest(int c, int cpr, int m) {
-    const int t = c / cpr;
+    const int t = row_of(c, cpr);
     const int q = c - t * cpr;
     const int kb = q >> 3, w8 = q & 7;
     return ((kb * 2 + (w8 >> 2)) * 4 + (w8 & 3)) * m + t;
@@ -192,26 +209,30 @@ struct XStage {
   // further): piece ((kb * 4 + 2h + part) * 4 + grp) * m + t holds the eight
   // values MFMA step 2h + part of lane group grp reads in K block kb.
   __device__ __forceinline__ static int dest16(int c, int cpr, int m) {
-    const int t = c / cpr;
+    const int t = row_of(c, cpr);
     const int q = c - t * cpr;
     const int kb = q >> 3, w8 = q & 7;
     return ((kb * 4 + 2 * (w8 >> 2)) * 4 + (w8 & 3)) * m + t;
   }
   __device__ __forceinline__ static uint4 src(const uint8_t* x, int K, size_t k0, int c, int cpr) {
-    const int t = c / cpr;
+    const int t = row_of(c, cpr);
     const int q = c - t * cpr;
     return *reinterpret_cast<const uint4*>(x + (size_t)t * K + k0 + 16 * q);
   }
   // Loads are issued for every thread (an index past the slice re-reads the
   // last chunk), so each wave issues the same number of loads and the
   // compiler can wait for exactly these, not for the W loads issued later.
-  __device__ __forceinline__ void load(const uint8_t* x, int K, size_t k0, int m, int cpr,
-                                       int xch, int c0, int tid) {
+  __device__ __forceinline__ void load(const uint8_t* x, int K, size_t k0, int cpr, int xch,
+                                       int c0, int tid) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int c = c0 + i * NT + tid;
       v[i] = src(x, K, k0, c < xch ? c : xch - 1, cpr);
     }
+  }
+  // The LDS places of the chunks (-1 past the slice): computed after the
+  // loads are issued, so that the W prologue goes out right after them.
+  __device__ __forceinline__ void dests(int m, int cpr, int xch, int c0, int tid) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int c = c0 + i * NT + tid;
@@ -225,7 +246,7 @@ struct XStage {
     for (int i = 0; i < kChunks; ++i) {
       int c = c0 + i * NT + tid;
       c = c < xch ? c : xch - 1;
-      const int t = c / cpr;
+      const int t = row_of(c, cpr);
       const int q = c - t * cpr;
       sc[i] = xs[(size_t)t * (K >> 5) + (k0 >> 5) + (q >> 1)];
     }
@@ -235,10 +256,11 @@ struct XStage {
                                               int nw, int c0, int tid) {
     const int c_0 = c0 + tid, c_1 = c0 + NT + tid;
     const int u0 = c_0 < nw ? c_0 : nw - 1, u1 = c_1 < nw ? c_1 : nw - 1;
-    s0 = *reinterpret_cast<const uint32_t*>(xs + (size_t)(u0 / wpr) * (K >> 5) + (k0 >> 5) +
-                                            4 * (u0 % wpr));
-    s1 = *reinterpret_cast<const uint32_t*>(xs + (size_t)(u1 / wpr) * (K >> 5) + (k0 >> 5) +
-                                            4 * (u1 % wpr));
+    const int t0 = row_of(u0, wpr), t1 = row_of(u1, wpr);
+    s0 = *reinterpret_cast<const uint32_t*>(xs + (size_t)t0 * (K >> 5) + (k0 >> 5) +
+                                            4 * (u0 - t0 * wpr));
+    s1 = *reinterpret_cast<const uint32_t*>(xs + (size_t)t1 * (K >> 5) + (k0 >> 5) +
+                                            4 * (u1 - t1 * wpr));
     e0 = c_0 < nw ? c_0 : -1;
     e1 = c_1 < nw ? c_1 : -1;
   }
@@ -260,11 +282,17 @@ struct XStage {
   __device__ __forceinline__ bool scales_out() const {
     bool out = false;
     if constexpr (X16) {
-      // A chunk of zero codes contributes zeros at any scale.
+      // A chunk of zero codes contributes zeros at any scale. The codes are
+      // looked at only when some scale byte of the wave is out of range.
+      bool sout = false;
 #pragma unroll
-      for (int i = 0; i < kChunks; ++i)
-        out |= d[i] >= 0 && scale_byte_out(sc[i]) &&
-               ((v[i].x | v[i].y | v[i].z | v[i].w) & 0x7F7F7F7Fu) != 0;
+      for (int i = 0; i < kChunks; ++i) sout |= d[i] >= 0 && scale_byte_out(sc[i]);
+      if (__any(sout)) {
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i)
+          out |= d[i] >= 0 && scale_byte_out(sc[i]) &&
+                 ((v[i].x | v[i].y | v[i].z | v[i].w) & 0x7F7F7F7Fu) != 0;
+      }
     } else {
       out = (e0 >= 0 && scale_word_out(s0)) || (e1 >= 0 && scale_word_out(s1));
     }
@@ -313,7 +341,7 @@ struct XQuant {
       if (c0 + i * NT + wbase >= xch8) break;
       int c = c0 + i * NT + tid;
       c = c < xch8 ? c : xch8 - 1;
-      const int t = c / cpr8;
+      const int t = row_of(c, cpr8);
       const int q = c - t * cpr8;
       v[i] = *reinterpret_cast<const uint4*>(xb + (size_t)t * K + k0 + 8 * q);
     }
@@ -340,7 +368,7 @@ struct XQuant {
         // where a code of 256 at scale byte 247 makes 2^128. Only the top
         // end of the range leaves BF16 here.
         out |= sb > kScaleHi;
-        const int t = c / cpr8;
+        const int t = row_of(c, cpr8);
         const int q = c - t * cpr8;
         if constexpr (X16) {
           // The codes' exact BF16 values: one piece (see XStage::dest16).
@@ -393,8 +421,9 @@ __device__ __attribute__((noinline)) bool stage_rest(const uint8_t* x, const uin
   XStage<NT, XR, X16> st;
   bool out = false;
   for (int c0 = c_first; c0 < xch; c0 += XStage<NT, XR>::kChunks * NT) {
-    st.load(x, K, k0, m, cpr, xch, c0, tid);
+    st.load(x, K, k0, cpr, xch, c0, tid);
     if constexpr (X16) st.load_chunk_scales(xs, K, k0, cpr, xch, c0, tid);
+    st.dests(m, cpr, xch, c0, tid);
     st.store(xl, m);
     if constexpr (X16) out |= st.scales_out();
   }
@@ -434,7 +463,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   // Wave-uniform in a scalar register, so the W stream's base addresses and
   // the per-block selects stay on the scalar unit.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool ctl = wave >= NT / 64;     // the control wave (split-K only)
+  const bool ctl = SK > 1 && wave >= NT / 64;  // the control wave (split-K only)
   const int hand_tid = SK > 1 ? NT : 0; // reads the hand-off words
   const int wn = wave % WN;
   const int wk = wave / WN;
@@ -471,8 +500,9 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   // ---- call hand-off: generation and epoch ------------------------------
   // Read once per workgroup, before it counts itself (all_gather page,
   // _AllGatherKernel.kernel: the last CTA to arrive advances the state).
-  // Without split-K one worker thread issues the generation load here and
-  // waits for it only where it stores it to LDS, after its x staging. With
+  // Without split-K every worker reads the generation with a scalar load
+  // (nothing writes it during the call) and one thread stores it to LDS
+  // after its x staging. With
   // split-K the control wave reads the generation, the epoch and the
   // workspace's error word (once a split-K poll has given up, its pairs can
   // no longer be told from this call's, so no later call publishes until
@@ -481,8 +511,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   // control wave's path joins the workers' would make the workers wait for
   // their whole W prologue at the first register they reuse.
   uint32_t gen = 0, epoch = 0;
-  if (S == 1 && tid == hand_tid && a.state)
-    gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
+  if (S == 1 && a.state) gen = ld_uniform_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
   if (S > 1 && tid == hand_tid) {
     if (a.state) gen = ld_agent_u32(a.state + MXG_STATE_NEXT) % MXG_GENERATIONS;
     epoch = ld_agent_u32(a.ws_hdr + MXG_WS_EPOCH) + a.epoch_bias;
@@ -499,22 +528,15 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   // mxgemm_pack_weight leaves one word per 16-row block after the tiles: the
   // smallest and largest scale byte (bits 0-7, 8-15) of the block's 32-wide
   // blocks that hold a nonzero code (0xFF and 0 when none does: a block of
-  // zero codes contributes zeros at any scale). Loaded before the x loads,
-  // so waiting for x covers it.
+  // zero codes contributes zeros at any scale). Loaded first in the worker
+  // region below, before the x loads, so waiting for x covers it.
   const int KBT = K >> 7;         // K blocks per row block
   const int rbn = (N + 15) >> 4;  // packed row blocks
+  const uint32_t* wsum = reinterpret_cast<const uint32_t*>(a.ws + (size_t)rbn * KBT * 64);
   uint32_t wrange[RB];
   int wshift[RB];  // the scale shift of each row block (0 inside the exact range)
 #pragma unroll
   for (int i = 0; i < RB; ++i) wshift[i] = 0;
-  if (!ctl) {
-    const uint32_t* wsum = reinterpret_cast<const uint32_t*>(a.ws + (size_t)rbn * KBT * 64);
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int rb = (row0 >> 4) + wn * RB + i;
-      wrange[i] = wsum[rb < rbn ? rb : rbn - 1];
-    }
-  }
 
   // ---- x slice, first round: loads issued before the W stream -----------
   const int cpr = KS >> 4;  // 16-byte chunks per x row in the slice
@@ -526,17 +548,6 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   XStage<NT, XR, X16> xst;
   XQuant<NT, X16> xqs;
   bool xout = false;  // an x scale byte this thread stages lies outside the exact range
-  if (!ctl) {
-    if constexpr (QX) {
-      xqs.load(a.xb, K, kslice0, cpr8, xch8, 0, tid);
-    } else {
-      xst.load(a.x, K, kslice0, m, cpr, xch, 0, tid);
-      if constexpr (X16)
-        xst.load_chunk_scales(a.xs, K, kslice0, cpr, xch, 0, tid);
-      else
-        xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
-    }
-  }
 
   // ---- W stream prologue (packed tiles, see mxgemm_pack_weight) ---------
   // Tile (rb, kb) is 2048 contiguous bytes: lane l's K pieces at 16 l and
@@ -581,6 +592,24 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   constexpr int G = D > 16 ? D : 16;  // K blocks per straight-line group
   const int ng0 = nbw < G ? nbw : G;
   if (!ctl) {
+    // The range words, x, then the W prologue, in one worker-only region: a
+    // load left in flight where the control wave's path joins would have
+    // the workers wait for their W prologue at the first register that load
+    // wrote.
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int rb = (row0 >> 4) + wn * RB + i;
+      wrange[i] = wsum[rb < rbn ? rb : rbn - 1];
+    }
+    if constexpr (QX) {
+      xqs.load(a.xb, K, kslice0, cpr8, xch8, 0, tid);
+    } else {
+      xst.load(a.x, K, kslice0, cpr, xch, 0, tid);
+      if constexpr (X16)
+        xst.load_chunk_scales(a.xs, K, kslice0, cpr, xch, 0, tid);
+      else
+        xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) load_w(d, d < ng0 ? d : -1);
 
@@ -600,6 +629,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
                                     XQuant<NT>::kChunks * NT);
     } else {
       uint32_t* xsw = reinterpret_cast<uint32_t*>(xsl);
+      xst.dests(m, cpr, xch, 0, tid);
       xst.pin_scales();
       xst.store(xl, m);
       if constexpr (!X16) xst.store_scales(xsw);
@@ -620,6 +650,8 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       asm volatile("" : "+v"(wrange[i]));
+      // The same word in every lane: worked on by the scalar unit.
+      wrange[i] = __builtin_amdgcn_readfirstlane(wrange[i]);
       const int lo = (int)(wrange[i] & 0xFFu), hi = (int)((wrange[i] >> 8) & 0xFFu);
       const int sh = lo < (int)kScaleLo ? (int)kScaleLo - lo
                                         : (hi > (int)kScaleHi ? (int)kScaleHi - hi : 0);
