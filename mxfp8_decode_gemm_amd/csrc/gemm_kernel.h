@@ -610,8 +610,14 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
       else
         xst.load_scales(a.xs, K, kslice0, wpr, nsw, 0, tid);
     }
+    // The ring in slot order (the scheduler would otherwise reorder the
+    // loads, and the in-order completion count would then make the first
+    // steps wait for the last slots).
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_w(d, d < ng0 ? d : -1);
+    for (int d = 0; d < D; ++d) {
+      load_w(d, d < ng0 ? d : -1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     // ---- x and its scales into LDS -------------------------------------
     // The x loads were issued first, so waiting for them leaves the W
@@ -855,6 +861,10 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
       if (j0 + 1 < nbw) consume_exact(el[1], eh[1], es[1], j0 + 1);
       eload(1, j0 + 3 < nbw ? j0 + 3 : -1);
     }
+    // No load of this path left in flight where it joins the main loop's:
+    // the compiler would otherwise make the main loop wait for its own W
+    // prologue before reusing those registers.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   } else {
     stream(consume);
     // Undo the row blocks' scale shifts: one rounding, FP32 subnormals kept.

@@ -217,9 +217,15 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, const char* t
   static const TileCfg kSplit[] = {{1, 7, 1, 5}, {1, 4, 1, 3}, {1, 2, 2, 5}, {1, 7, 1, 3},
                                    {1, 2, 2, 8}, {1, 7, 1, 4}, {1, 4, 1, 8}, {1, 4, 2, 8},
                                    {2, 1, 4, 4}, {1, 1, 4, 4}};
+  // Without split-K the 16- and 8-wave 16-row tiles tie in the cost below;
+  // measured on N=4096/K=16384, the 8-wave one is faster up to 4 tokens
+  // (m=1: 14.9 against 16.6 us, m=4: 16.1 against 16.8 us) and the 16-wave
+  // one at 8 (17.4 against 18.2 us).
   static const TileCfg kNoSplit[] = {{1, 1, 16, 4}, {1, 1, 8, 4}, {1, 2, 2, 5}, {1, 2, 2, 8},
                                      {1, 4, 1, 3}, {1, 1, 4, 4}, {2, 1, 4, 4}};
-  const TileCfg* list = split_k > 1 ? kSplit : kNoSplit;
+  static const TileCfg kNoSplitFew[] = {{1, 1, 8, 4}, {1, 1, 16, 4}, {1, 2, 2, 5}, {1, 2, 2, 8},
+                                        {1, 4, 1, 3}, {1, 1, 4, 4}, {2, 1, 4, 4}};
+  const TileCfg* list = split_k > 1 ? kSplit : (m <= 4 ? kNoSplitFew : kNoSplit);
   const size_t count = split_k > 1 ? sizeof(kSplit) / sizeof(kSplit[0])
                                    : sizeof(kNoSplit) / sizeof(kNoSplit[0]);
   constexpr double kGroupCost = 32768.0;  // bytes-equivalent fixed cost per workgroup
