@@ -84,8 +84,8 @@ def _check(raw, got, p, bitwise):
 @pytest.mark.parametrize("scales", [(57, 57), (1, 118), (118, 1)])
 def test_negative_zero_reaches_the_epilogue(env, scales, split_k, x16, monkeypatch):
     """Products of +-2^-140 (scale bytes 57 and 57: the main loop) and
-    +-2^-135 (1 and 118, 118 and 1: the exact path) are the only term of
-    their outputs. The raw output holds BF16 -0 (0x8000) for the negative ones
+    +-2^-135 (1 and 118: the W row block shifted into range; 118 and 1: the
+    exact path) are the only term of their outputs. The raw output holds BF16 -0 (0x8000) for the negative ones
     and +0 for the positive ones; the mailbox holds 0x0000 for both."""
     if x16 == "0":
         monkeypatch.setattr(env[0], "TILE", "fp8")
