@@ -1050,7 +1050,9 @@ struct Variant {
   Variant{TileCfg{RB, WN, WK, D}, SK, MXG_FN(RB, WN, WK, D, SK, false, 1, false),    \
           MXG_FN(RB, WN, WK, D, SK, true, 1, false),                                 \
           MXG_FN(RB, WN, WK, D, SK, false, 1, true), MXG_FN(RB, WN, WK, D, SK, true, 1, true)}
-// The two-round x stage (xr = 2); BF16 x stages through XQuant either way.
+// The x stage with an 8-chunk first round (xr = 2: a slice of twice the
+// size staged before the first barrier without a second, out-of-line round);
+// BF16 x stages through XQuant either way.
 // Not built with x staged as BF16: on C3's m = 8, split-K 4 shape that was
 // 1 us slower.
 #define MXG_V2(RB, WN, WK, D, SK)                                                    \

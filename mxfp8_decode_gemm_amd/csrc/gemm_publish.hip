@@ -244,8 +244,9 @@ static bool choose_tile_uncached(int m, int n, int k, int split_k, const char* t
     }
   }
   // A slice of x that needs more than one staging round of 4 chunks per
-  // thread: the variant with a two-round first stage, when built and resident
-  // (on C3's m = 8, S = 4 shape it measured 17.5 -> 16.8 us).
+  // thread: the variant with an 8-chunk first round, when built and resident
+  // (N=4096/K=16384/m=8: S=4 17.5 -> 16.8 us; S=1 on the 16-wave tile
+  // 18.6 -> 18.0 us).
   if (found) {
     const long chunks = (long)m * (ks / 16);
     TileCfg c2 = *out;

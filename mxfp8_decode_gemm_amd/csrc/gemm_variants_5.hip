@@ -13,6 +13,7 @@ const Variant kPart[] = {
     MXG_V2(1, 4, 1, 3, 2),
     MXG_V2(1, 4, 1, 3, 4),
     MXG_V2(1, 4, 1, 3, 8),
+    MXG_V2(1, 1, 16, 4, 1),
 };
 }  // namespace
 

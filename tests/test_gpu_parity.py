@@ -126,7 +126,7 @@ def test_rows_and_ragged_n(env, m):
 # kept as BF16 in LDS (without it: BF16 when it fits, the default).
 TILES = ["1,1,4,4", "1,1,8,4", "1,1,16,4", "1,4,1,8", "1,4,1,3", "1,7,1,8", "1,7,1,4",
          "1,7,1,3", "1,7,1,5", "1,2,2,8", "1,2,2,5", "1,4,2,8", "2,1,4,4", "1,8,1,8", "2,2,2,4",
-         "1,4,1,3,2",  # two-round activation stage
+         "1,4,1,3,2", "1,1,16,4,2",  # one staging round of twice the size
          # x left in FP8 in LDS, converted by every wave
          "1,1,4,4,1,0", "1,1,16,4,1,0", "1,4,1,3,1,0", "1,7,1,3,1,0", "1,2,2,8,1,0",
          "1,4,1,3,2,0",
