@@ -84,7 +84,8 @@ def parse() -> argparse.Namespace:
                     help="the plain read of one packed W copy in every organisation "
                          "mxg_stream_read_cfg offers, one line each")
     ap.add_argument("--tile-sweep", default="",
-                    help="comma-separated configuration names (C0, C1, C2, C3-m1-s4, C4-A, "
+                    help="comma-separated workload names as --all-configs prints them "
+                         "(n7168_k2048_m4, n4096_k16384_m1_s4, stress_n2048_k8192_m8_s4, "
                          "... or all): every built GEMM variant's time on each")
     ap.add_argument("--activation-quant", action="store_true",
                     help="time the BF16-activation and unfused-publish variants, one line each")
@@ -573,15 +574,18 @@ def config_cases():
     configuration."""
     from workloads import generate
 
-    cases = [("C0", generate.config_problem(0), 1, 512, 100),
-             ("C1", generate.config_problem(1), 1, 57344, 3),
-             ("C2", generate.config_problem(2), 1, 114688, 3),
-             ("C2-normal", generate.config_problem(2, dist="normal"), 1, 114688, 3)]
+    cases = [("n256_k512_m1", generate.config_problem(0), 1, 512, 100),
+             ("n7168_k2048_m4", generate.config_problem(1), 1, 57344, 3),
+             ("n7168_k8192_m8_s4", generate.config_problem(2), 1, 114688, 3),
+             ("n7168_k8192_m8_s4_normal", generate.config_problem(2, dist="normal"), 1, 114688,
+              3)]
     for m in (1, 2, 4, 8):
         for s in (1, 4, 8):
-            cases.append((f"C3-m{m}-s{s}", generate.config_problem(3, m=m, split_k=s), 4, 65536, 3))
+            cases.append((f"n4096_k16384_m{m}_s{s}", generate.config_problem(3, m=m, split_k=s),
+                          4, 65536, 3))
     for size in (0, 1):
-        cases.append((f"C4-{'AB'[size]}", generate.config_problem(4, size=size), 4, 32768, 3))
+        p4 = generate.config_problem(4, size=size)
+        cases.append((f"stress_n{p4.n}_k{p4.k}_m{p4.m}_s{p4.split_k}", p4, 4, 32768, 3))
     return cases
 
 

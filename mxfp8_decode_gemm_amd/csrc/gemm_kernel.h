@@ -1053,7 +1053,7 @@ struct Variant {
 // The x stage with an 8-chunk first round (xr = 2: a slice of twice the
 // size staged before the first barrier without a second, out-of-line round);
 // BF16 x stages through XQuant either way.
-// Not built with x staged as BF16: on C3's m = 8, split-K 4 shape that was
+// Not built with x staged as BF16: on N=4096/K=16384/m=8/split-K 4 that was
 // 1 us slower.
 #define MXG_V2(RB, WN, WK, D, SK)                                                    \
   Variant{TileCfg{RB, WN, WK, D, 2}, SK, MXG_FN(RB, WN, WK, D, SK, false, 2, false), \

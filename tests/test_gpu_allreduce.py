@@ -111,7 +111,7 @@ def test_allreduce_spin_limit_sets_error(env):
 
 
 def test_allreduce_alternating_sizes_in_graphs(env):
-    """Config 4's alternating sizes through one mailbox with the all-reduce
+    """The stress workload's alternating sizes through one mailbox with the all-reduce
     collect, 1000 calls per graph replayed 20 times, every output compared
     on the device with the verified one of its size."""
     from test_gpu_parity import graph_soak

@@ -97,7 +97,7 @@ def run_case(env, p, split_k=1, ranks=1, capacity=None, peers=None, calls=1, wit
     return own, bits, ex
 
 
-def test_tiny_config(env):
+def test_n256_k512_m1(env):
     from workloads import generate
 
     run_case(env, generate.config_problem(0), calls=4)
@@ -279,14 +279,14 @@ def test_fused_equals_unfused(env):
     assert torch.equal(oa, ob)
 
 
-def test_config1_full(env):
+def test_n7168_k2048_m4(env):
     from workloads import generate
 
     run_case(env, generate.config_problem(1))
 
 
 @pytest.mark.parametrize("dist", ["outliers", "normal"])
-def test_config2_full(env, dist):
+def test_n7168_k8192_m8_s4(env, dist):
     from workloads import generate
 
     p = generate.config_problem(2, dist=dist)
@@ -295,7 +295,7 @@ def test_config2_full(env, dist):
 
 @pytest.mark.parametrize("m", [1, 2, 4, 8])
 @pytest.mark.parametrize("split_k", [1, 4, 8])
-def test_config3_sweep(env, m, split_k):
+def test_n4096_k16384_sweep(env, m, split_k):
     from workloads import generate
 
     p = generate.config_problem(3, m=m, split_k=split_k)
@@ -303,7 +303,7 @@ def test_config3_sweep(env, m, split_k):
     run_case(env, p, split_k=split_k, ranks=4, capacity=65536, peers=peers, calls=4)
 
 
-def test_config4_alternating(env):
+def test_stress_alternating(env):
     """Alternating sizes through one mailbox and one workspace: every output
     bit-identical to the first verified output of its size, nothing stale."""
     mx, dv = env
@@ -577,8 +577,8 @@ def graph_soak(env, probs, split_k, ranks, capacity, per_graph, replays, ws_n=No
 
 @pytest.mark.parametrize("m", [1, 2, 4, 8])
 @pytest.mark.parametrize("split_k", [1, 4, 8])
-def test_config3_graph_1000_calls(env, m, split_k):
-    """Config 3 as stated: 1000 back-to-back calls in one HIP graph, four
+def test_n4096_k16384_graph_1000_calls(env, m, split_k):
+    """N=4096, K=16384 at every m and split: 1000 back-to-back calls in one HIP graph, four
     emulated rank slots, the three generations cycling."""
     from workloads import generate
 
@@ -587,8 +587,8 @@ def test_config3_graph_1000_calls(env, m, split_k):
 
 
 @pytest.mark.parametrize("dist", ["outliers", "normal"])
-def test_config2_graph_100_calls(env, dist):
-    """Config 2 as stated: the epoch advances once per call over 100
+def test_n7168_k8192_m8_s4_graph_100_calls(env, dist):
+    """N=7168, K=8192, m=8, split-K 4: the epoch advances once per call over 100
     graph-captured calls, every output identical to the verified one."""
     from workloads import generate
 
@@ -596,8 +596,9 @@ def test_config2_graph_100_calls(env, dist):
     graph_soak(env, [p], 4, 1, 114688, per_graph=100, replays=1)
 
 
-def test_config4_million_alternating_calls(env):
-    """Config 4 at full count: 10^6 alternating-size calls (GEMM+publish into
+def test_stress_million_alternating_calls(env):
+    """The stress workload at full count: 10^6 calls alternating N=7168/K=4096/m=1
+    and N=2048/K=8192/m=8 at split-K 4 (GEMM+publish into
     slot 0, three emulated peers, collect) through one mailbox and one
     workspace, in HIP graphs of 1000 calls replayed 1000 times: zero
     mismatched and zero sentinel words, the mailbox idle and the state words

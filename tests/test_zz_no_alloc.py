@@ -71,7 +71,7 @@ def _compare(env, p, split_k, calls=1):
 
 
 def test_noalloc_matches_publish_two_calls(env):
-    """C2's shape (N=7168, K=8192, m=8, split-K 4), then a smaller one (N=1000,
+    """N=7168, K=8192, m=8, split-K 4, then a smaller one (N=1000,
     K=2048, m=3, split-K 8) that reuses the pair addresses of the first."""
     from workloads import generate
 
