@@ -49,5 +49,6 @@ def test_traffic_comes_from_a_matching_profile():
 def test_help_lists_the_modes():
     r = _run("--help")
     assert r.returncode == 0
-    for flag in ("--all-configs", "--collectives", "--activation-quant", "--steps"):
+    for flag in ("--all-configs", "--collectives", "--activation-quant", "--stream-sweep",
+                 "--tile-sweep", "--skip-warm", "--steps"):
         assert flag in r.stdout
