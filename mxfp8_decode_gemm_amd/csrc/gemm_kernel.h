@@ -145,6 +145,12 @@ constexpr int kLoadNontemporal = 2;
 __device__ __forceinline__ uint32_t ld_uniform_u32(const uint32_t* p) {
   return *(const __attribute__((address_space(4))) uint32_t*)(p);
 }
+// Lane i takes lane i + N of its 16-lane row (0 where that lies past the
+// row): a DPP move on the vector unit instead of an LDS permute.
+template <int N>
+__device__ __forceinline__ uint32_t row_down(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x100 + N, 0xF, 0xF, true);
+}
 __device__ __forceinline__ uint32_t ld_agent_u32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -997,15 +1003,16 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
       // gathered into lane e = 0: raw store, negative-zero clear, publish.
       const __bf16 hb = (__bf16)v;
       const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, hb);
-      const uint32_t pair = h | ((uint32_t)__shfl_down(h, 1, 64) << 16);
-      const uint32_t p1 = __shfl_down(pair, 2, 64);
-      const uint32_t p2 = __shfl_down(pair, 4, 64);
-      const uint32_t p3 = __shfl_down(pair, 6, 64);
+      // (Lane e = 0 of a pack reads lanes 1..7 of its own 8, inside its row.)
+      const uint32_t pair = h | (row_down<1>(h) << 16);
+      const uint32_t p1 = row_down<2>(pair);
+      const uint32_t p2 = row_down<4>(pair);
+      const uint32_t p3 = row_down<6>(pair);
       // A pack with a column whose poll gave up is not published.
       uint32_t fp = failed ? 1u : 0u;
-      fp |= __shfl_down(fp, 1, 64);
-      fp |= __shfl_down(fp, 2, 64);
-      fp |= __shfl_down(fp, 4, 64);
+      fp |= row_down<1>(fp);
+      fp |= row_down<2>(fp);
+      fp |= row_down<4>(fp);
       if (live && e == 0 && fp == 0 && !ws_failed) {
         const uint4 raw = {pair, p1, p2, p3};
         const size_t off = ((size_t)t * N + row0 + 8 * jc) * 2;
