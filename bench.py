@@ -486,7 +486,7 @@ def headline(args) -> int:
             for i in range(3):
                 warm.step(i)
             torch.cuda.synchronize()
-            warm_ms = gemm_only_ms(warm, K)
+            warm_ms = gemm_only_ms(warm, KL)
         del warm
 
     algo = p.algorithmic_bytes()
@@ -603,6 +603,7 @@ def all_configs(args) -> int:
     from workloads import generate
 
     K = args.steps
+    KL = max(10 * K, 100)  # launches per graph for the per-launch figures
     for name, p, ranks, cap, cpu_calls in config_cases():
         peers = generate.peer_payloads(p.seed, ranks, p.m, p.n) if ranks > 1 else None
         run = Runner(p, p.split_k, ranks, cap, args.cold_mib, peers)
@@ -612,13 +613,13 @@ def all_configs(args) -> int:
             torch.cuda.synchronize()
             # One untimed pass first: the first graph timed after the setup
             # runs slower (0.4-0.7 us on the larger shapes).
-            gemm_only_ms(run, K)
-            kern_ms = gemm_only_ms(run, K)
+            gemm_only_ms(run, KL)
+            kern_ms = gemm_only_ms(run, KL)
             step_ms = run.graph_ms(lambda: [run.step(i) for i in range(K)], K, timed=3)
             ok = run.state_ok()
-            read_ms, read_bytes = stream_ms(run, K)
-            best_ms, _ = stream_ms(run, K, BEST_STREAM)
-            floor_ms = launch_floor_ms(run, K)
+            read_ms, read_bytes = stream_ms(run, KL)
+            best_ms, _ = stream_ms(run, KL, BEST_STREAM)
+            floor_ms = launch_floor_ms(run, KL)
         del run
         torch.cuda.empty_cache()
         warm = Runner(p, p.split_k, ranks, cap, 0, peers)
@@ -626,7 +627,7 @@ def all_configs(args) -> int:
             for i in range(3):
                 warm.step(i)
             torch.cuda.synchronize()
-            warm_ms = gemm_only_ms(warm, K)
+            warm_ms = gemm_only_ms(warm, KL)
         del warm
         torch.cuda.empty_cache()
         algo = p.algorithmic_bytes()
@@ -671,6 +672,7 @@ def tile_sweep(args) -> int:
 
     wanted = set(args.tile_sweep.split(","))
     K = args.steps
+    KL = max(10 * K, 100)  # launches per graph
     for name, p, ranks, cap, _ in config_cases():
         if name not in wanted and "all" not in wanted:
             continue
@@ -683,7 +685,7 @@ def tile_sweep(args) -> int:
             # One untimed pass first: the first graph timed after the setup
             # runs slower (0.4-0.7 us on the larger shapes), whatever the tile.
             mx.TILE = None
-            gemm_only_ms(run, K)
+            gemm_only_ms(run, KL)
             for tile in [None] + SWEEP_TILES:
                 mx.TILE = tile
                 try:
@@ -692,7 +694,7 @@ def tile_sweep(args) -> int:
                 except mx.MxgUnsupported:
                     continue
                 torch.cuda.synchronize()
-                ms = gemm_only_ms(run, K)
+                ms = gemm_only_ms(run, KL)
                 ok = run.state_ok()
                 res.append((tile or "default", ms))
                 print(json.dumps({"mode": "tile_sweep", "config": name, "tile": tile or "default",
