@@ -14,9 +14,9 @@ from the 256 MiB Infinity Cache.
 The timed region is one replay of a HIP graph holding the K steps back to
 back (the decode loop as it is served); `value` is algorithmic bytes per step
 over the replay's time per step. The GEMM kernel's own time per launch comes
-from a graph of 10 K back-to-back GEMM+publish launches (so the graph's own
-launch latency, about 25 us before its first kernel, weighs 0.2 % per
-launch), HIP events around each of three replays on the launch stream (the
+from a graph of 10 x K back-to-back GEMM+publish launches (1000 at the
+default K, so the graph's own launch latency, about 25 us before its first
+kernel, weighs 0.2 % per launch), HIP events around each of three replays on the launch stream (the
 median); the roofline compares
 algorithmic bytes per launch over it with the 8 TB/s HBM peak. Also printed: the same with one W
 copy (Infinity-Cache warm), the events attached to each eager launch, the
@@ -528,7 +528,7 @@ def headline(args) -> int:
             "traffic": traffic_from_profile(),
         },
         "stream_context": {
-            "what": "plain HBM read of one packed W copy (mxg_stream_read), graph of 10 K launches "
+            "what": f"plain HBM read of one packed W copy (mxg_stream_read), graph of {KL} launches "
                     "over the same rotating copies: the achievable read rate at this size",
             "bytes": read_bytes,
             "us": round(read_ms * 1e3, 3),
