@@ -93,6 +93,10 @@ extern "C" {
 #define MXG_ERR_COLLECT_SPIN 0x1u /* a collect gave up polling a slot */
 #define MXG_ERR_SPLITK_SPIN 0x2u  /* a split-K owner gave up polling its pairs */
 
+/* Default poll limit of the device waits (MXG_DEFAULT_SPIN_LIMIT polls, with
+ * s_sleep between polls). */
+#define MXG_DEFAULT_SPIN_LIMIT (1u << 20)
+
 /* Host-side descriptor of one mailbox (plain data, copied freely). */
 typedef struct mxg_mailbox {
   void* slots;             /* device: 3 * ranks * capacity_bytes, 16-B aligned */
@@ -100,6 +104,11 @@ typedef struct mxg_mailbox {
   int32_t ranks;           /* emulated rank slots, 1..8 */
   int32_t rank;            /* the slot mxgemm_publish writes, 0..ranks-1 */
   int64_t capacity_bytes;  /* bytes per rank slot, > 0, multiple of 16 */
+  uint32_t spin_limit;     /* polls before a device wait of a call on this
+                              mailbox gives up (its collect, its split-K
+                              exchange); 0: MXG_DEFAULT_SPIN_LIMIT. mailbox_init
+                              sets 0; tests set it small to force a time-out */
+  uint32_t reserved;       /* 0 */
 } mxg_mailbox;
 
 /* Bytes of slot memory a mailbox needs: 3 * ranks * capacity_bytes, or 0 if
@@ -209,7 +218,7 @@ int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int3
  * keep FP32 subnormals; a result or partial sum beyond the FP32 range is
  * infinite or NaN on any, as FP32 accumulation gives.
  *
- * Failure: a split-K poll that gives up (see mxg_set_spin_limit) sets
+ * Failure: a split-K poll that gives up (after mb->spin_limit polls) sets
  * MXG_ERR_SPLITK_SPIN in the workspace's ERROR word and leaves its packs
  * unpublished (c_out unwritten there), and every later call on that
  * workspace reads the bit and publishes nothing, so the collect that follows
@@ -224,12 +233,11 @@ int mxgemm_pack_weight(const uint8_t* w, const uint8_t* w_scale, int32_t n, int3
  * to rounding, not bit for bit. For measurement and tests mxgemm_tile runs
  * the same GEMM with a chosen variant; the library reads no environment.
  *
- * Host state: the library keeps no configuration between calls except the
- * poll limit of mxg_set_spin_limit (a process-wide debugging knob, read at
- * launch; a deliberate departure from a fully stateless interface: the
- * limit only decides when a wait that should never be long gives up) and
- * memos of device queries (the default tile per shape and device, the
- * resident-workgroup counts, the no-allocation scratch's device address),
+ * Host state: the library keeps no configuration between calls. The poll
+ * limit travels in the caller's mxg_mailbox; mxgemm, which has none, polls
+ * its split-K pairs up to MXG_DEFAULT_SPIN_LIMIT times. What the library does
+ * keep are memos of device queries (the default tile per shape and device,
+ * the resident-workgroup counts, the no-allocation scratch's device address),
  * which change no result. */
 int mxgemm_publish(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
                    const uint8_t* x, const uint8_t* x_scale, int32_t m, int32_t n,
@@ -374,7 +382,7 @@ int mailbox_all_gather(const mxg_mailbox* mb, const void* src, void* out, int64_
  * payload), and store the sentinel back; state[NEXT] becomes (g + 1) mod 3
  * (step 3). The owner's publish (mxgemm_publish or mailbox_publish into slot
  * mb->rank) must precede the collect on its stream. A pack still holding a sentinel after
- * the spin limit is copied as it is and MXG_ERR_COLLECT_SPIN is set in
+ * mb->spin_limit polls is copied as it is and MXG_ERR_COLLECT_SPIN is set in
  * state[ERROR]. `out` is device memory of ranks * nbytes bytes, 16-B aligned.
  * Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY, MXG_EHIP. */
 int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream);
@@ -388,7 +396,7 @@ int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stre
  * and the sums are rounded once to BF16 (nearest even) into out + 16 p
  * ([m, n] BF16 for an [m, n] payload; a sum can round to negative zero).
  * Every rank's pack is reset to the sentinel and the generation advances as
- * in mailbox_collect; a pack still holding a sentinel after the spin limit
+ * in mailbox_collect; a pack still holding a sentinel after mb->spin_limit polls
  * sets MXG_ERR_COLLECT_SPIN. `out` is device memory of nbytes bytes, 16-B
  * aligned. Errors: MXG_EINVAL, MXG_EALIGN, MXG_ECAPACITY, MXG_EHIP. */
 int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream);
@@ -438,11 +446,6 @@ int mxg_stream_read_cfg(const void* src, size_t bytes, uint32_t* sink, int32_t w
  * any address. Errors: MXG_EINVAL, MXG_EALIGN, MXG_EHIP. */
 int mxg_probe_mfma(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
                    const uint8_t* b_scale, int32_t k, int32_t scaled, float* c, void* stream);
-
-/* Poll limit of the device spin loops (collect and split-K), in polls; the
- * loops back off with s_sleep between polls. Returns the previous limit.
- * A limit of 0 restores the default (2^20 polls). Process-wide. */
-uint32_t mxg_set_spin_limit(uint32_t polls);
 
 /* HIP graph helpers: capture the calls issued on `stream` between begin and
  * end into an executable graph, replay it, destroy it. `exec` is an opaque

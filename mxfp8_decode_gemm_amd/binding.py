@@ -71,6 +71,8 @@ class mxg_mailbox(ctypes.Structure):
         ("ranks", ctypes.c_int32),
         ("rank", ctypes.c_int32),
         ("capacity_bytes", ctypes.c_int64),
+        ("spin_limit", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
     ]
 
 
@@ -109,7 +111,6 @@ def _load() -> ctypes.CDLL:
                                        i32, vp, sz, vp, vp, vp, vp]),
         "mxfp8_quantize": (ctypes.c_int, [vp, i32, i32, vp, vp, vp]),
         "mailbox_all_gather": (ctypes.c_int, [mbp, vp, vp, i64, vp]),
-        "mxg_set_spin_limit": (u32, [u32]),
         "mxg_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
         "mxg_probe_mfma": (ctypes.c_int, [vp, vp, vp, vp, i32, i32, vp, vp]),
         "mxg_stream_read_cfg": (ctypes.c_int, [vp, sz, vp, i32, i32, i32, i32, i32, vp]),
@@ -356,10 +357,6 @@ def mxg_stream_read_cfg(src, nbytes: int, sink, workgroups: int, threads: int, u
 def mxg_stream_read(src, nbytes: int, sink, stream=None) -> None:
     _check(_lib.mxg_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
            "mxg_stream_read")
-
-
-def mxg_set_spin_limit(polls: int) -> int:
-    return int(_lib.mxg_set_spin_limit(polls))
 
 
 def mxg_graph_begin(stream=None) -> None:

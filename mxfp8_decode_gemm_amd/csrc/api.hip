@@ -5,7 +5,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstdint>
 
 #include "../../include/mxgemm.h"
@@ -13,8 +12,6 @@
 
 namespace mxg {
 namespace {
-std::atomic<uint32_t> g_spin_limit{1u << 20};
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool mailbox_ok(const mxg_mailbox* mb) {
@@ -26,7 +23,9 @@ bool mailbox_ok(const mxg_mailbox* mb) {
 int hip_code(hipError_t e) { return e == hipSuccess ? MXG_OK : MXG_EHIP; }
 }  // namespace
 
-uint32_t spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+uint32_t spin_limit(const mxg_mailbox* mb) {
+  return mb && mb->spin_limit ? mb->spin_limit : MXG_DEFAULT_SPIN_LIMIT;
+}
 }  // namespace mxg
 
 using namespace mxg;
@@ -55,6 +54,8 @@ int mailbox_init(mxg_mailbox* mb, void* slots, uint32_t* state, int32_t ranks, i
   mb->ranks = ranks;
   mb->rank = rank;
   mb->capacity_bytes = capacity_bytes;
+  mb->spin_limit = 0;
+  mb->reserved = 0;
   return MXG_OK;
 }
 
@@ -170,7 +171,7 @@ int gemm_call(const mxg_mailbox* mb, const uint8_t* w, const uint8_t* w_scale,
   a.n = n;
   a.k = k;
   a.split_k = split_k;
-  a.spin_limit = spin_limit();
+  a.spin_limit = spin_limit(mb);
   a.epoch_bias = epoch_bias;
   return hip_code(launch_gemm_publish(a, cfg, static_cast<hipStream_t>(stream),
                                       static_cast<hipEvent_t>(ev_start),
@@ -276,7 +277,7 @@ int mailbox_all_gather(const mxg_mailbox* mb, const void* src, void* out, int64_
   return hip_code(launch_mailbox_all_gather(
       static_cast<uint8_t*>(mb->slots), (int64_t)mb->ranks * mb->capacity_bytes,
       mb->capacity_bytes, mb->ranks, mb->rank, mb->state, s, static_cast<uint8_t*>(out),
-      nbytes, spin_limit(), static_cast<hipStream_t>(stream)));
+      nbytes, spin_limit(mb), static_cast<hipStream_t>(stream)));
 }
 
 int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream) {
@@ -287,7 +288,7 @@ int mailbox_collect(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stre
   return hip_code(launch_mailbox_collect(
       static_cast<uint8_t*>(mb->slots), (int64_t)mb->ranks * mb->capacity_bytes,
       mb->capacity_bytes, mb->ranks, mb->state, static_cast<uint8_t*>(out), nbytes,
-      spin_limit(), static_cast<hipStream_t>(stream)));
+      spin_limit(mb), static_cast<hipStream_t>(stream)));
 }
 
 int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* stream) {
@@ -298,7 +299,7 @@ int mailbox_collect_sum(const mxg_mailbox* mb, void* out, int64_t nbytes, void* 
   return hip_code(launch_mailbox_collect_sum(
       static_cast<uint8_t*>(mb->slots), (int64_t)mb->ranks * mb->capacity_bytes,
       mb->capacity_bytes, mb->ranks, mb->state, static_cast<uint8_t*>(out), nbytes,
-      spin_limit(), static_cast<hipStream_t>(stream)));
+      spin_limit(mb), static_cast<hipStream_t>(stream)));
 }
 
 int mxg_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
@@ -331,10 +332,6 @@ int mxg_probe_mfma(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
   if (!aligned16(a) || !aligned16(b) || !aligned16(c)) return MXG_EALIGN;
   return hip_code(launch_mfma_probe(a, a_scale, b, b_scale, k, scaled, c,
                                     static_cast<hipStream_t>(stream)));
-}
-
-uint32_t mxg_set_spin_limit(uint32_t polls) {
-  return g_spin_limit.exchange(polls == 0 ? (1u << 20) : polls);
 }
 
 int mxg_graph_begin(void* stream) {

@@ -119,7 +119,8 @@ hipError_t launch_mailbox_all_gather(uint8_t* slots, int64_t gen_stride, int64_t
                                      uint8_t* out, int64_t nbytes, uint32_t spin_limit,
                                      hipStream_t s);
 
-uint32_t spin_limit();
+// Poll limit of a call on mailbox mb (null: the default).
+uint32_t spin_limit(const mxg_mailbox* mb);
 
 // Host validation of a GEMM call from sizes and addresses alone, everything
 // but the workspace: MXG_OK or the code gemm_call would return.

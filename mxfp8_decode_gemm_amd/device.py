@@ -45,6 +45,16 @@ class Mailbox:
         self.mb = mx.mailbox_init(self.slots, self.state, self.ranks, self.rank,
                                   self.capacity_bytes, stream)
 
+    @property
+    def spin_limit(self) -> int:
+        """Polls before a device wait of a call on this mailbox gives up (0:
+        the library's default); carried in the descriptor, read at launch."""
+        return int(self.mb.spin_limit)
+
+    @spin_limit.setter
+    def spin_limit(self, polls: int) -> None:
+        self.mb.spin_limit = polls
+
     def state_words(self) -> np.ndarray:
         return self.state.cpu().numpy().view(np.uint32).copy()
 

@@ -22,7 +22,7 @@ def mx():
 
 def test_exports_every_declared_function(mx):
     names = mx.header_functions()
-    assert len(names) == 28
+    assert len(names) == 27
     lib = mx.library()
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing
@@ -139,8 +139,10 @@ def test_pack_sizes_and_validation(mx):
 def test_misc(mx):
     lib = mx.library()
     assert mx.strerror(0) == "ok" and "aligned" in mx.strerror(-2)
-    prev = mx.mxg_set_spin_limit(123)
-    assert mx.mxg_set_spin_limit(prev) == 123
+    # the descriptor as the header declares it: the poll limit travels in it
+    assert ctypes.sizeof(mx.mxg_mailbox) == 40
+    assert mx.mxg_mailbox.spin_limit.offset == 32 and mx.mxg_mailbox.reserved.offset == 36
+    assert not hasattr(lib, "mxg_set_spin_limit")  # no process-wide knob
     assert lib.mxg_graph_begin(None) == -1
     assert lib.mxg_graph_launch(None, None) == -1
     assert lib.mxg_graph_destroy(None) == -1

@@ -154,12 +154,9 @@ def test_all_gather_spin_limit_sets_error(env):
 
     mbx = dv.Mailbox(2, 256, rank=1)
     src = torch.ones(32, dtype=torch.int32, device="cuda")
-    prev = mx.mxg_set_spin_limit(8)
-    try:
-        dv.all_gather(mbx, src, 128)
-        torch.cuda.synchronize()
-    finally:
-        mx.mxg_set_spin_limit(prev)
+    mbx.spin_limit = 8
+    dv.all_gather(mbx, src, 128)
+    torch.cuda.synchronize()
     assert mbx.state_words()[mx.STATE_ERROR] & mx.ERR_COLLECT_SPIN
     assert not mailbox.check_idle_slots(mbx.slot_words())
 

@@ -100,12 +100,9 @@ def test_allreduce_spin_limit_sets_error(env):
 
     mbx = dv.Mailbox(2, 256)
     mx.mailbox_publish(mbx.mb, 0, torch.ones(64, dtype=torch.int16, device="cuda"), 128)
-    prev = mx.mxg_set_spin_limit(8)
-    try:
-        dv.collect_sum(mbx, 128)
-        torch.cuda.synchronize()
-    finally:
-        mx.mxg_set_spin_limit(prev)
+    mbx.spin_limit = 8
+    dv.collect_sum(mbx, 128)
+    torch.cuda.synchronize()
     assert mbx.state_words()[mx.STATE_ERROR] & mx.ERR_COLLECT_SPIN
     assert not mailbox.check_idle_slots(mbx.slot_words())
 

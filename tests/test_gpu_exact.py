@@ -337,25 +337,19 @@ def test_splitk_timeout_is_fatal_to_the_workspace(env):
     # With a poll limit of 1 a wait gives up unless its words are already
     # there at the first look, which a call can happen to meet everywhere:
     # calls (each one published and collected) until one gives up.
-    prev = mx.mxg_set_spin_limit(1)
-    try:
-        for _ in range(16):
-            dv.publish(mbx, ops, 4, ws, c)
-            dv.collect(mbx, p.out_bytes)
-            torch.cuda.synchronize()
-            if ws.header()[mx.WS_ERROR] & mx.ERR_SPLITK_SPIN:
-                break
-    finally:
-        mx.mxg_set_spin_limit(prev)
+    mbx.spin_limit = 1
+    for _ in range(16):
+        dv.publish(mbx, ops, 4, ws, c)
+        dv.collect(mbx, p.out_bytes)
+        torch.cuda.synchronize()
+        if ws.header()[mx.WS_ERROR] & mx.ERR_SPLITK_SPIN:
+            break
     assert ws.header()[mx.WS_ERROR] & mx.ERR_SPLITK_SPIN
     # the next call: nothing published, the collect gives up (short limit)
-    prev = mx.mxg_set_spin_limit(256)
-    try:
-        dv.publish(mbx, ops, 4, ws, c)
-        out = dv.collect(mbx, p.out_bytes)
-        torch.cuda.synchronize()
-    finally:
-        mx.mxg_set_spin_limit(prev)
+    mbx.spin_limit = 256
+    dv.publish(mbx, ops, 4, ws, c)
+    out = dv.collect(mbx, p.out_bytes)
+    torch.cuda.synchronize()
     words = out.view(torch.int32).cpu().numpy().view(np.uint32)
     assert np.all(words == 0x80000000)
     assert mbx.state_words()[mx.STATE_ERROR] & mx.ERR_COLLECT_SPIN

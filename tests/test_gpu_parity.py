@@ -391,12 +391,9 @@ def test_collect_spin_limit_sets_error(env):
     mbx = dv.Mailbox(2, 256)
     src = torch.ones(64, dtype=torch.int16, device="cuda")
     mx.mailbox_publish(mbx.mb, 0, src, 128)
-    prev = mx.mxg_set_spin_limit(8)
-    try:
-        dv.collect(mbx, 128)
-        torch.cuda.synchronize()
-    finally:
-        mx.mxg_set_spin_limit(prev)
+    mbx.spin_limit = 8
+    dv.collect(mbx, 128)
+    torch.cuda.synchronize()
     st = mbx.state_words()
     assert st[mx.STATE_ERROR] & mx.ERR_COLLECT_SPIN
     assert not mailbox.check_idle_slots(mbx.slot_words())
