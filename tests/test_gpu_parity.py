@@ -402,6 +402,39 @@ def test_collect_spin_limit_sets_error(env):
     assert mbx.state_words()[mx.STATE_ERROR] == 0
 
 
+def test_stray_word_is_reported_by_the_idle_scan(env):
+    """A non-sentinel word written from the host into the next generation's
+    slot, past the bytes the next call publishes and collects, is what a
+    missed reset would leave (all_gather page, module docstring, step 2: no
+    call leaves a word for a later one). The collect of that smaller call
+    neither reads nor resets it, and the post-collect scan of the whole
+    mailbox reports it; the call's own output stays exact. Arming again
+    clears it."""
+    mx, dv = env
+    _, gemm, mailbox, tolerance = _oracle()
+    from workloads import generate
+
+    p = generate.random_problem(4343, 2, 64, 256)  # 256 bytes of output
+    ops = dv.Operands(p)
+    mbx = dv.Mailbox(1, 1024)
+    assert not mailbox.check_idle_slots(mbx.slot_words())
+    # generation 0, the one the next publish uses; word 128 lies past 256 bytes
+    mbx.slots[128] = 0x12345678
+    c = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
+    dv.publish(mbx, ops, 1, None, c)
+    out = dv.as_u16(dv.collect(mbx, p.out_bytes)).reshape(p.m, p.n)
+    torch.cuda.synchronize()
+    _, exact, abs_sum = gemm.gemm_publish_bits(p.w, p.ws, p.x, p.xs)
+    assert tolerance.within(out, exact, abs_sum)
+    assert not mailbox.check_collected(out)
+    words = mbx.slot_words()
+    assert mailbox.check_idle_slots(words)
+    assert words[0, 0, 128] == 0x12345678 and np.count_nonzero(words != 0x80000000) == 1
+    mbx.reinit()
+    torch.cuda.synchronize()
+    assert not mailbox.check_idle_slots(mbx.slot_words())
+
+
 def test_stale_epoch_is_not_taken(env):
     """Pairs left by an earlier call never carry the live tag: after a call of
     one size, a call of another size that reuses the same pair addresses still
