@@ -42,7 +42,7 @@ the last output against the CPU oracle, and the oracle's time per call.
 (mxfp8_quantize, then mxgemm_publish), and the publish fused into the GEMM
 against the page's unfused path (mxgemm writes C, mailbox_publish reads it
 back). Each variant: a graph of K whole steps (with the collect) and a graph
-of K launches of its kernels alone.
+of 10 x K launches of its kernels alone.
 """
 
 from __future__ import annotations
@@ -856,6 +856,7 @@ def activation_quant(args) -> int:
     c = torch.empty(p.m * p.n, dtype=torch.int16, device="cuda")
     wsb, wsn = run.wsp.buf, run.wsp.nbytes
     K = args.steps
+    KL = max(10 * K, 100)  # launches per graph for the kernel figures
 
     def w(i):
         return run.w[i % run.copies]
@@ -893,12 +894,12 @@ def activation_quant(args) -> int:
                 body(i)
                 run.collect()
             torch.cuda.synchronize()
-            # kernels alone: K back-to-back calls, the mailbox drained after
-            # each replay (every call republishes into the same generation);
-            # one untimed pass first (the first graph timed after a setup runs
-            # slower)
-            run.graph_ms(lambda: [body(i) for i in range(K)], K, after=run.collect)
-            kern_ms = run.graph_ms(lambda: [body(i) for i in range(K)], K, after=run.collect,
+            # kernels alone: 10 x K back-to-back calls, the mailbox drained
+            # after each replay (every call republishes into the same
+            # generation); one untimed pass first (the first graph timed after
+            # a setup runs slower)
+            run.graph_ms(lambda: [body(i) for i in range(KL)], KL, after=run.collect)
+            kern_ms = run.graph_ms(lambda: [body(i) for i in range(KL)], KL, after=run.collect,
                                    timed=3)
             step_ms = run.graph_ms(lambda: [(body(i), run.collect()) for i in range(K)], K,
                                    timed=3)
