@@ -596,7 +596,8 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     }
   };
   constexpr int G = D > 16 ? D : 16;  // K blocks per straight-line group
-  constexpr int DX = QX && SK > 1 && D > 3 ? 3 : D;  // ring slots issued before the x stage
+  // Ring slots issued before the x stage (the rest follow it).
+  constexpr int DX = SK > 1 && D > 3 && (QX || WN * WK <= 4) ? 3 : D;
   const int ng0 = nbw < G ? nbw : G;
   if (!ctl) {
     // The range words, x, then the W prologue, in one worker-only region: a
@@ -619,11 +620,14 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     }
     // The ring in slot order (the scheduler would otherwise reorder the
     // loads, and the in-order completion count would then make the first
-    // steps wait for the last slots). BF16 x with split-K issues only DX
-    // slots here and the rest after its stage: twice the activation bytes
-    // then land sooner, and the W stream still has three slots in flight
-    // (N=7168/K=8192/m=8/S=4: 15.5 -> 15.0 us; N=2048/K=8192/m=8/S=4 10.5 ->
-    // 10.3 us; without split-K, N=7168/K=2048/m=4, it was 0.07 us slower).
+    // steps wait for the last slots). With split-K, BF16 x and tiles of at
+    // most four worker waves issue only DX slots here and the rest after
+    // the x stage: x then lands sooner and the W stream still has three
+    // slots in flight. Interleaved A/B: BF16 x N=7168/K=8192/m=8/S=4 15.5 ->
+    // 15.0 us, N=2048/K=8192/m=8/S=4 10.5 -> 10.3 us; MXFP8 x on the 4-wave
+    // tile of N=2048/K=8192/m=8/S=4 7.40 -> 7.08 us (mean of 9). The 7-wave
+    // tile of N=7168/K=8192/m=8/S=4 and N=7168/K=4096/m=1/S=4 was level or
+    // 0.1 us slower, and without split-K (N=7168/K=2048/m=4) 0.07 us slower.
 #pragma unroll
     for (int d = 0; d < DX; ++d) {
       load_w(d, d < ng0 ? d : -1);
@@ -660,6 +664,11 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
         xout |= stage_rest<NT, XR, X16>(a.x, a.xs, K, kslice0, m, cpr, xch, wpr, nsw, tid, xl,
                                         xsw, XStage<NT, XR>::kChunks * NT,
                                         XStage<NT, XR>::kWords * NT);
+#pragma unroll
+      for (int d = DX; d < D; ++d) {
+        load_w(d, d < ng0 ? d : -1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // Range flags of this wave. The W summary is pinned here so that its
     // use, and so the wait for it, stays behind the W prologue. A row block
