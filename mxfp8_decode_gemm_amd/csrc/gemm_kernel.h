@@ -597,7 +597,7 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
   };
   constexpr int G = D > 16 ? D : 16;  // K blocks per straight-line group
   // Ring slots issued before the x stage (the rest follow it).
-  constexpr int DX = SK > 1 && D > 3 && (QX || WN * WK <= 4) ? 3 : D;
+  constexpr int DX = SK == 1 ? (WN * WK >= 8 ? 1 : D) : (D > 3 && (QX || WN * WK <= 4) ? 3 : D);
   const int ng0 = nbw < G ? nbw : G;
   if (!ctl) {
     // The range words, x, then the W prologue, in one worker-only region: a
@@ -620,14 +620,18 @@ __global__ void __launch_bounds__(64 * (WN * WK + (SK > 1 ? 1 : 0)))
     }
     // The ring in slot order (the scheduler would otherwise reorder the
     // loads, and the in-order completion count would then make the first
-    // steps wait for the last slots). With split-K, BF16 x and tiles of at
-    // most four worker waves issue only DX slots here and the rest after
-    // the x stage: x then lands sooner and the W stream still has three
-    // slots in flight. Interleaved A/B: BF16 x N=7168/K=8192/m=8/S=4 15.5 ->
-    // 15.0 us, N=2048/K=8192/m=8/S=4 10.5 -> 10.3 us; MXFP8 x on the 4-wave
-    // tile of N=2048/K=8192/m=8/S=4 7.40 -> 7.08 us (mean of 9). The 7-wave
-    // tile of N=7168/K=8192/m=8/S=4 and N=7168/K=4096/m=1/S=4 was level or
-    // 0.1 us slower, and without split-K (N=7168/K=2048/m=4) 0.07 us slower.
+    // steps wait for the last slots). Some tiles issue only DX slots here
+    // and the rest after the x stage, so that x lands sooner; the W stream
+    // still has slots in flight meanwhile. Interleaved A/B:
+    //  * split-K, BF16 x and tiles of at most four worker waves, 3 slots:
+    //    BF16 x N=7168/K=8192/m=8/S=4 15.5 -> 15.0 us, N=2048/K=8192/m=8/S=4
+    //    10.5 -> 10.3 us; MXFP8 x on the 4-wave tile of N=2048/K=8192/m=8/S=4
+    //    7.40 -> 7.08 us (mean of 9). The 7-wave tile of N=7168/K=8192/m=8/S=4
+    //    and N=7168/K=4096/m=1/S=4 was level or 0.1 us slower;
+    //  * without split-K, tiles of 8 or more waves (a whole-K x stage), 1
+    //    slot: N=4096/K=16384 m=4 16.0 -> 15.3 us, m=8 17.2 -> 16.6 us, m=1
+    //    and m=2 level (2 slots: bimodal, often slower); the 4-wave tile of
+    //    N=7168/K=2048/m=4 was level or slower and keeps all its slots.
 #pragma unroll
     for (int d = 0; d < DX; ++d) {
       load_w(d, d < ng0 ? d : -1);
