@@ -34,8 +34,9 @@
 //     (measured), so the B operand uses the same K split.
 //   * x and its scales for the workgroup's K slice are staged once in LDS, in
 //     the order the B operand reads them, and shared by every wave; their
-//     loads go out before the W prologue and are waited for after it (XR sets
-//     how many chunks each thread loads in that first round). With BF16 x
+//     loads go out before the W prologue and are waited for after it, or
+//     after its first DX slots on the tiles that issue the rest later (XR
+//     sets how many chunks each thread loads in that first round). With BF16 x
 //     (QX) the stage quantizes it to e4m3 codes and E8M0 scales on the way
 //     (quant_device.h). Variants built with X16 store the slice as its
 //     exact BF16 values instead (each chunk converted with its scale byte on
